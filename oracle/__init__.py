@@ -1,0 +1,200 @@
+"""Plain fp64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the GPU library and never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over heads or
+rows); this module builds and loads it with ctypes and marshals numpy arrays.
+What each function computes, with its source passages, is stated in the
+header of ``oracle.c``: the three-step definition S = QK^T, P = softmax(S),
+O = PV of the lab write-up (section 2.1), its analytic backward, the
+online-softmax recurrence of section 3.2, and Philox-4x32-10 dropout bits.
+
+Layout: tensors are float64 numpy arrays [tokens, H, d]; a fixed-length batch
+[B, N, H, d] is passed reshaped to [B*N, H, d].  Sequence s covers tokens
+``starts[s] .. starts[s] + lens[s] - 1``.  LSE is [tokens, H].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_keep.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int]
+        lib.oracle_keep.restype = ctypes.c_int
+        lib.oracle_keep_mask.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.POINTER(ctypes.c_uint8)]
+        lib.oracle_keep_mask.restype = None
+        common = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                  ctypes.c_double, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int, ip]
+        lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp] + common
+        lib.oracle_fwd.restype = None
+        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp] + common
+        lib.oracle_bwd.restype = None
+        lib.oracle_fwd_head_tiled.argtypes = [dp, dp, dp, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_double, ctypes.c_int, ctypes.c_double,
+                                              ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp,
+                                              ctypes.c_long]
+        lib.oracle_fwd_head_tiled.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dptr(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _iptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+
+
+def dropout_threshold(p: float) -> int:
+    """floor(p * 2^32) for the float32 value of p (an element is kept iff its
+    Philox word is >= this threshold)."""
+    return int(math.floor(float(np.float32(p)) * 4294967296.0))
+
+
+def _seq_layout(tokens: int, N: int | None, lengths):
+    if lengths is None:
+        assert tokens % N == 0
+        nseq = tokens // N
+        starts = np.arange(nseq, dtype=np.int32) * N
+        lens = np.full(nseq, N, dtype=np.int32)
+    else:
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+        starts = np.zeros(len(lens), dtype=np.int32)
+        if len(lens) > 1:
+            starts[1:] = np.cumsum(lens[:-1])
+        assert int(lens.sum()) == tokens
+    return starts, lens
+
+
+def _sel(heads):
+    if heads is None:
+        return 0, None
+    a = np.ascontiguousarray(np.asarray(heads, dtype=np.int32).reshape(-1, 2))
+    return a.shape[0], a
+
+
+def _prep(*xs):
+    return [np.ascontiguousarray(x, dtype=np.float64) for x in xs]
+
+
+def forward(q, k, v, *, scale: float, causal: bool, N: int | None = None, lengths=None,
+            dropout_p: float = 0.0, seed: int = 0, heads=None):
+    """O and LSE of attention.  q, k, v: float64 [tokens, H, d].
+
+    Fixed length: pass N (sequence length; tokens = B*N).  Varlen: pass the
+    list of sequence lengths.  ``heads`` = optional list of (sequence, head)
+    pairs to compute; other entries of O and LSE are returned as NaN.
+    Dropout keep bits depend on (seed, sequence index, head, row, col)."""
+    lib = _load()
+    q, k, v = _prep(q, k, v)
+    T, H, d = q.shape
+    starts, lens = _seq_layout(T, N, lengths)
+    nsel, sel = _sel(heads)
+    o = np.full_like(q, np.nan)
+    lse = np.full((T, H), np.nan, dtype=np.float64)
+    lib.oracle_fwd(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse), len(lens), _iptr(starts),
+                   _iptr(lens), H, d, float(scale), int(bool(causal)), float(np.float32(dropout_p)),
+                   dropout_threshold(dropout_p) if dropout_p > 0 else 0, int(seed) & (2**64 - 1),
+                   nsel, _iptr(sel))
+    return o, lse
+
+
+def backward(q, k, v, dout, *, scale: float, causal: bool, N: int | None = None, lengths=None,
+             dropout_p: float = 0.0, seed: int = 0, heads=None):
+    """dQ, dK, dV of L = sum(O * dout), with O = forward(q, k, v)."""
+    lib = _load()
+    q, k, v, dout = _prep(q, k, v, dout)
+    T, H, d = q.shape
+    starts, lens = _seq_layout(T, N, lengths)
+    nsel, sel = _sel(heads)
+    dq = np.full_like(q, np.nan)
+    dk = np.full_like(q, np.nan)
+    dv = np.full_like(q, np.nan)
+    lib.oracle_bwd(_dptr(q), _dptr(k), _dptr(v), _dptr(dout), _dptr(dq), _dptr(dk), _dptr(dv),
+                   len(lens), _iptr(starts), _iptr(lens), H, d, float(scale), int(bool(causal)),
+                   float(np.float32(dropout_p)), dropout_threshold(dropout_p) if dropout_p > 0 else 0,
+                   int(seed) & (2**64 - 1), nsel, _iptr(sel))
+    return dq, dk, dv
+
+
+def forward_tiled_head(q, k, v, *, scale: float, causal: bool, Br: int, Bc: int,
+                       dropout_p: float = 0.0, seed: int = 0, b: int = 0, h: int = 0):
+    """Online-softmax recurrence (fp64) on one head; q, k, v: [L, d]."""
+    lib = _load()
+    q, k, v = _prep(q, k, v)
+    L, d = q.shape
+    o = np.zeros_like(q)
+    lse = np.zeros(L, dtype=np.float64)
+    lib.oracle_fwd_head_tiled(_dptr(q), _dptr(k), _dptr(v), d, L, d, float(scale), int(bool(causal)),
+                              float(np.float32(dropout_p)),
+                              dropout_threshold(dropout_p) if dropout_p > 0 else 0,
+                              int(seed) & (2**64 - 1), b, h, Br, Bc, _dptr(o), _dptr(lse), 1)
+    return o, lse
+
+
+def philox4x32_10(counter, key):
+    """Raw Philox-4x32-10 block: four uint32 words for a 4-word counter and 2-word key."""
+    lib = _load()
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in counter])
+    kk = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    lib.oracle_philox4x32_10(c, kk, out)
+    return [int(x) for x in out]
+
+
+def keep(seed: int, thresh: int, b: int, h: int, i: int, j: int) -> bool:
+    """Keep bit of one element for an explicit threshold (kept iff word >= thresh)."""
+    return bool(_load().oracle_keep(int(seed) & (2**64 - 1), int(thresh), b, h, i, j))
+
+
+def keep_mask(seed: int, dropout_p: float, b: int, h: int, L: int) -> np.ndarray:
+    """Dropout keep mask (uint8, 1 = kept) of one head, [L, L] (rows = queries)."""
+    lib = _load()
+    m = np.zeros((L, L), dtype=np.uint8)
+    lib.oracle_keep_mask(int(seed) & (2**64 - 1), dropout_threshold(dropout_p), b, h, L,
+                         m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    return m
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())

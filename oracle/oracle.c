@@ -1,0 +1,378 @@
+/*
+ * Plain fp64 CPU oracle for exact scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant generator
+ * with the GPU library.
+ *
+ * What it computes follows the three-step definition of attention on the
+ * page "企业官网建设流程全解析" (dpshk.com lab write-up), section 2.1
+ * ("三步计算背后的显存账本"): S = Q K^T, P = row softmax(S), O = P V, with
+ * the scale 1/sqrt(d) applied to S as in the einsum reference of the
+ * tiemojia.cn article ("scores = einsum(bthd,bshd->bhts)/sqrt_d").  Tensors
+ * use the [batch, seq, heads, head_dim] layout named in section 4.2 of the
+ * lab write-up.  Each (sequence, head) pair is computed on its own:
+ *
+ *   step 1  S[i][j] = scale * sum_c q[i][c] k[j][c]   for visible j
+ *   step 2  P[i][j] = exp(S[i][j] - m_i) / sum_j' exp(S[i][j'] - m_i)
+ *           (m_i = row max; a full two-pass softmax over the whole row)
+ *           LSE_i   = m_i + ln sum_j exp(S[i][j] - m_i)
+ *   dropout Z[i][j] = P[i][j] * keep(i,j) / (1 - p)   (else Z = P)
+ *   step 3  O[i]    = sum_j Z[i][j] v[j]
+ *
+ * "Visible" means j <= i for causal attention, every j < L otherwise.
+ * The N x N matrices S, P (and dP in the backward) are materialised per
+ * head on purpose: this is the standard algorithm the tiled method is
+ * exactly equivalent to (lab write-up section 3.2).
+ *
+ * The backward is the textbook analytic gradient of L = sum O*dO:
+ *   dZ[i][j] = dO_i . v_j,  dP[i][j] = dZ[i][j] * keep/(1-p)
+ *   dS[i][j] = P[i][j] (dP[i][j] - sum_k P[i][k] dP[i][k])
+ *   dQ_i = scale sum_j dS[i][j] k_j,  dK_j = scale sum_i dS[i][j] q_i,
+ *   dV_j = sum_i Z[i][j] dO_i.
+ *
+ * oracle_fwd_head_tiled() runs the online-softmax recurrences of the lab
+ * write-up, section 3.2 (running row max m and row sum l, O rescaled by
+ * e^{m - m_new} per column block, divided by l at the end), in fp64.  It
+ * exists only to check that the tiled recurrence equals the definition.
+ *
+ * Dropout keep bits come from Philox-4x32-10 (Salmon, Moraes, Dror, Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11), written here from
+ * that paper: key = (seed low word, seed high word); counter =
+ * (row i, col j / 4, head h, batch-or-sequence b); column j uses output word
+ * j mod 4; the element is kept iff that word >= thresh, where the caller
+ * passes thresh = floor(p * 2^32).  Row and column indices are local to the
+ * sequence.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- Philox */
+
+static void philox_round(uint32_t c[4], uint32_t k0, uint32_t k1)
+{
+    uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c[0];
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c[2];
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    uint32_t n0 = hi1 ^ c[1] ^ k0;
+    uint32_t n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+}
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {            /* Weyl key schedule between rounds */
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        philox_round(c, k0, k1);
+    }
+    memcpy(out, c, sizeof(c));
+}
+
+int oracle_keep(uint64_t seed, uint32_t thresh, int b, int h, int i, int j)
+{
+    uint32_t ctr[4] = {(uint32_t)i, (uint32_t)j >> 2, (uint32_t)h, (uint32_t)b};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return out[j & 3] >= thresh;
+}
+
+/* Keep mask of one (b, h) head, row-major L x L bytes (1 = kept). */
+void oracle_keep_mask(uint64_t seed, uint32_t thresh, int b, int h, int L, uint8_t* mask)
+{
+    for (int i = 0; i < L; ++i)
+        for (int j = 0; j < L; ++j)
+            mask[(size_t)i * L + j] = (uint8_t)oracle_keep(seed, thresh, b, h, i, j);
+}
+
+/* --------------------------------------------------------- common pieces */
+
+typedef struct {
+    double scale;     /* multiplies q.k */
+    int causal;
+    int dropout;      /* 0: no dropout */
+    double keep_scale;/* 1/(1-p) */
+    uint32_t thresh;  /* floor(p * 2^32) */
+    uint64_t seed;
+    int b, h;         /* counter indices of this head */
+} head_args;
+
+static int n_visible(const head_args* a, int i, int L) { return a->causal ? i + 1 : L; }
+
+static double dot(const double* x, const double* y, int d)
+{
+    double s = 0.0;
+    for (int c = 0; c < d; ++c) s += x[c] * y[c];
+    return s;
+}
+
+/* Steps 1 and 2 for one head: fills P (L x L, zero where not visible) and lse. */
+static void softmax_rows(const double* q, const double* k, long ld, int L, int d,
+                         const head_args* a, double* P, double* lse)
+{
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int i = 0; i < L; ++i) {
+        double* row = P + (size_t)i * L;
+        int nv = n_visible(a, i, L);
+        double m = -INFINITY;
+        for (int j = 0; j < nv; ++j) {
+            row[j] = a->scale * dot(q + (size_t)i * ld, k + (size_t)j * ld, d);
+            if (row[j] > m) m = row[j];
+        }
+        double sum = 0.0;
+        for (int j = 0; j < nv; ++j) sum += exp(row[j] - m);
+        for (int j = 0; j < nv; ++j) row[j] = exp(row[j] - m) / sum;
+        for (int j = nv; j < L; ++j) row[j] = 0.0;
+        if (lse) lse[i] = m + log(sum);
+    }
+}
+
+static double keep_factor(const head_args* a, int i, int j)
+{
+    if (!a->dropout) return 1.0;
+    return oracle_keep(a->seed, a->thresh, a->b, a->h, i, j) ? a->keep_scale : 0.0;
+}
+
+/* --------------------------------------------------------------- forward */
+
+/* One head.  q, k, v, o point at row 0 of the head; rows are ld elements
+ * apart (ld = H*d for a [tokens, H, d] tensor).  lse is indexed lse[i*lse_ld]. */
+void oracle_fwd_head(const double* q, const double* k, const double* v, long ld, int L, int d,
+                     double scale, int causal, double dropout_p, uint32_t thresh, uint64_t seed,
+                     int b, int h, double* o, double* lse, long lse_ld)
+{
+    if (L <= 0) return;
+    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h};
+    double* P = (double*)malloc(sizeof(double) * (size_t)L * L);
+    double* l = (double*)malloc(sizeof(double) * (size_t)L);
+    softmax_rows(q, k, ld, L, d, &a, P, l);
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int i = 0; i < L; ++i) {
+        double* oi = o + (size_t)i * ld;
+        for (int c = 0; c < d; ++c) oi[c] = 0.0;
+        int nv = n_visible(&a, i, L);
+        for (int j = 0; j < nv; ++j) {
+            double z = P[(size_t)i * L + j] * keep_factor(&a, i, j);
+            const double* vj = v + (size_t)j * ld;
+            for (int c = 0; c < d; ++c) oi[c] += z * vj[c];
+        }
+        lse[(size_t)i * lse_ld] = l[i];
+    }
+    free(l);
+    free(P);
+}
+
+/* Online-softmax recurrence with Br x Bc blocks (fp64), for the
+ * tiled-equals-definition check only. */
+void oracle_fwd_head_tiled(const double* q, const double* k, const double* v, long ld, int L, int d,
+                           double scale, int causal, double dropout_p, uint32_t thresh, uint64_t seed,
+                           int b, int h, int Br, int Bc, double* o, double* lse, long lse_ld)
+{
+    if (L <= 0) return;
+    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h};
+    double* acc = (double*)malloc(sizeof(double) * (size_t)Br * d);
+    double* m = (double*)malloc(sizeof(double) * (size_t)Br);
+    double* l = (double*)malloc(sizeof(double) * (size_t)Br);
+    double* s = (double*)malloc(sizeof(double) * (size_t)Br * Bc);
+    for (int i0 = 0; i0 < L; i0 += Br) {
+        int nr = L - i0 < Br ? L - i0 : Br;
+        for (int r = 0; r < nr; ++r) { m[r] = -INFINITY; l[r] = 0.0; }
+        memset(acc, 0, sizeof(double) * (size_t)nr * d);
+        for (int j0 = 0; j0 < L; j0 += Bc) {
+            int nc = L - j0 < Bc ? L - j0 : Bc;
+            for (int r = 0; r < nr; ++r) {
+                int i = i0 + r;
+                /* S_ij block row and its local max over visible columns */
+                double bm = -INFINITY;
+                for (int t = 0; t < nc; ++t) {
+                    int j = j0 + t;
+                    if (causal && j > i) { s[(size_t)r * Bc + t] = -INFINITY; continue; }
+                    double sv = scale * dot(q + (size_t)i * ld, k + (size_t)j * ld, d);
+                    s[(size_t)r * Bc + t] = sv;
+                    if (sv > bm) bm = sv;
+                }
+                if (bm == -INFINITY) continue;          /* block fully masked for this row */
+                double m_new = m[r] > bm ? m[r] : bm;
+                double alpha = exp(m[r] - m_new);       /* e^{m - m_new}; 0 on the first block */
+                double* ar = acc + (size_t)r * d;
+                for (int c = 0; c < d; ++c) ar[c] *= alpha;
+                l[r] *= alpha;
+                for (int t = 0; t < nc; ++t) {
+                    double sv = s[(size_t)r * Bc + t];
+                    if (sv == -INFINITY) continue;
+                    double e = exp(sv - m_new);
+                    l[r] += e;                           /* l excludes dropout */
+                    double z = e * keep_factor(&a, i, j0 + t);
+                    const double* vj = v + (size_t)(j0 + t) * ld;
+                    for (int c = 0; c < d; ++c) ar[c] += z * vj[c];
+                }
+                m[r] = m_new;
+            }
+        }
+        for (int r = 0; r < nr; ++r) {
+            double* oi = o + (size_t)(i0 + r) * ld;
+            for (int c = 0; c < d; ++c) oi[c] = acc[(size_t)r * d + c] / l[r];
+            lse[(size_t)(i0 + r) * lse_ld] = m[r] + log(l[r]);
+        }
+    }
+    free(s); free(l); free(m); free(acc);
+}
+
+/* -------------------------------------------------------------- backward */
+
+void oracle_bwd_head(const double* q, const double* k, const double* v, const double* dout,
+                     long ld, int L, int d, double scale, int causal, double dropout_p,
+                     uint32_t thresh, uint64_t seed, int b, int h,
+                     double* dq, double* dk, double* dv)
+{
+    if (L <= 0) return;
+    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h};
+    size_t LL = (size_t)L * L;
+    double* P = (double*)malloc(sizeof(double) * LL);
+    double* dS = (double*)malloc(sizeof(double) * LL);
+    double* Z = (double*)malloc(sizeof(double) * LL);
+    softmax_rows(q, k, ld, L, d, &a, P, NULL);
+    /* dP and dS, one row at a time */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int i = 0; i < L; ++i) {
+        int nv = n_visible(&a, i, L);
+        double* dsr = dS + (size_t)i * L;
+        double* zr = Z + (size_t)i * L;
+        const double* pr = P + (size_t)i * L;
+        double rowdot = 0.0;
+        for (int j = 0; j < nv; ++j) {
+            double kf = keep_factor(&a, i, j);
+            double dp = dot(dout + (size_t)i * ld, v + (size_t)j * ld, d) * kf;
+            dsr[j] = dp;
+            zr[j] = pr[j] * kf;
+            rowdot += pr[j] * dp;
+        }
+        for (int j = 0; j < nv; ++j) dsr[j] = pr[j] * (dsr[j] - rowdot);
+        for (int j = nv; j < L; ++j) { dsr[j] = 0.0; zr[j] = 0.0; }
+    }
+    /* dQ = scale dS K */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int i = 0; i < L; ++i) {
+        double* g = dq + (size_t)i * ld;
+        for (int c = 0; c < d; ++c) g[c] = 0.0;
+        for (int j = 0; j < L; ++j) {
+            double w = dS[(size_t)i * L + j];
+            if (w == 0.0) continue;
+            const double* kj = k + (size_t)j * ld;
+            for (int c = 0; c < d; ++c) g[c] += w * kj[c];
+        }
+        for (int c = 0; c < d; ++c) g[c] *= scale;
+    }
+    /* dK = scale dS^T Q,  dV = Z^T dO */
+    #pragma omp parallel for schedule(dynamic, 8)
+    for (int j = 0; j < L; ++j) {
+        double* gk = dk + (size_t)j * ld;
+        double* gv = dv + (size_t)j * ld;
+        for (int c = 0; c < d; ++c) { gk[c] = 0.0; gv[c] = 0.0; }
+        for (int i = 0; i < L; ++i) {
+            double w = dS[(size_t)i * L + j];
+            double z = Z[(size_t)i * L + j];
+            const double* qi = q + (size_t)i * ld;
+            const double* gi = dout + (size_t)i * ld;
+            for (int c = 0; c < d; ++c) { gk[c] += w * qi[c]; gv[c] += z * gi[c]; }
+        }
+        for (int c = 0; c < d; ++c) gk[c] *= scale;
+    }
+    free(Z); free(dS); free(P);
+}
+
+/* ---------------------------------------------------- whole-batch drivers */
+
+/* Tensors are [tokens, H, d] (contiguous); sequence s occupies tokens
+ * starts[s] .. starts[s] + lens[s] - 1.  lse is [tokens, H].  If sel is not
+ * NULL only the nsel (sequence, head) pairs sel[2t], sel[2t+1] are computed;
+ * other outputs are left untouched. */
+static void run_pairs(int nseq, const int* starts, const int* lens, int H, int nsel, const int* sel,
+                      void (*fn)(int s, int h, void* ctx), void* ctx)
+{
+    int npairs = sel ? nsel : nseq * H;
+    if (npairs == 1) {               /* one head: let the head function use the threads */
+        fn(sel ? sel[0] : 0, sel ? sel[1] : 0, ctx);
+        return;
+    }
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < npairs; ++t) {
+        int s = sel ? sel[2 * t] : t / H;
+        int h = sel ? sel[2 * t + 1] : t % H;
+        fn(s, h, ctx);
+    }
+    (void)starts; (void)lens;
+}
+
+typedef struct {
+    const double *q, *k, *v, *dout;
+    double *o, *lse, *dq, *dk, *dv;
+    const int *starts, *lens;
+    int H, d, causal;
+    double scale, p;
+    uint32_t thresh;
+    uint64_t seed;
+} batch_ctx;
+
+static void fwd_one(int s, int h, void* vctx)
+{
+    batch_ctx* c = (batch_ctx*)vctx;
+    long ld = (long)c->H * c->d;
+    size_t off = (size_t)c->starts[s] * ld + (size_t)h * c->d;
+    oracle_fwd_head(c->q + off, c->k + off, c->v + off, ld, c->lens[s], c->d, c->scale, c->causal,
+                    c->p, c->thresh, c->seed, s, h, c->o + off,
+                    c->lse + (size_t)c->starts[s] * c->H + h, c->H);
+}
+
+static void bwd_one(int s, int h, void* vctx)
+{
+    batch_ctx* c = (batch_ctx*)vctx;
+    long ld = (long)c->H * c->d;
+    size_t off = (size_t)c->starts[s] * ld + (size_t)h * c->d;
+    oracle_bwd_head(c->q + off, c->k + off, c->v + off, c->dout + off, ld, c->lens[s], c->d,
+                    c->scale, c->causal, c->p, c->thresh, c->seed, s, h,
+                    c->dq + off, c->dk + off, c->dv + off);
+}
+
+void oracle_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
+                int nseq, const int* starts, const int* lens, int H, int d, double scale, int causal,
+                double dropout_p, uint32_t thresh, uint64_t seed, int nsel, const int* sel)
+{
+    batch_ctx c = {q, k, v, NULL, o, lse, NULL, NULL, NULL, starts, lens, H, d, causal,
+                   scale, dropout_p, thresh, seed};
+    run_pairs(nseq, starts, lens, H, nsel, sel, fwd_one, &c);
+}
+
+void oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
+                double* dq, double* dk, double* dv,
+                int nseq, const int* starts, const int* lens, int H, int d, double scale, int causal,
+                double dropout_p, uint32_t thresh, uint64_t seed, int nsel, const int* sel)
+{
+    batch_ctx c = {q, k, v, dout, NULL, NULL, dq, dk, dv, starts, lens, H, d, causal,
+                   scale, dropout_p, thresh, seed};
+    run_pairs(nseq, starts, lens, H, nsel, sel, bwd_one, &c);
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

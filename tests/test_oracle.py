@@ -1,0 +1,370 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: a hand-worked
+example, a closed form, an invariant the mathematics fixes, torch's own fp64
+scaled_dot_product_attention and autograd, central finite differences, and
+rocRAND's independent Philox-4x32-10 engine.
+"""
+import json
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def fwd(q, k, v, scale, causal, **kw):
+    """[L, d] single-head helper."""
+    o, lse = oracle.forward(q[:, None, :], k[:, None, :], v[:, None, :], scale=scale, causal=causal,
+                            N=q.shape[0], **kw)
+    return o[:, 0, :], lse[:, 0]
+
+
+def bwd(q, k, v, do, scale, causal, **kw):
+    g = oracle.backward(q[:, None, :], k[:, None, :], v[:, None, :], do[:, None, :], scale=scale,
+                        causal=causal, N=q.shape[0], **kw)
+    return [x[:, 0, :] for x in g]
+
+
+# ----------------------------------------------------------------- golden
+
+def test_hand_worked_two_token_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_two_token.json")))
+    x = g["inputs"]
+    q, k, v, do = (np.array(x[n], dtype=np.float64)[:, None] for n in ("q", "k", "v", "dout"))
+    for causal, key in ((False, "noncausal"), (True, "causal")):
+        o, lse = fwd(q, k, v, x["scale"], causal)
+        np.testing.assert_allclose(o[:, 0], g[key]["o"], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse, g[key]["lse"], rtol=0, atol=1e-14)
+    dq, dk, dv = bwd(q, k, v, do, x["scale"], False)
+    e = g["noncausal"]
+    np.testing.assert_allclose(dq[:, 0], e["dq"], atol=1e-14)
+    np.testing.assert_allclose(dk[:, 0], e["dk"], atol=1e-14)
+    np.testing.assert_allclose(dv[:, 0], e["dv"], atol=1e-14)
+
+
+# ----------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_mean_of_visible_values(causal):
+    L, d = 37, 8
+    q = np.zeros((L, d)); k = rnd((L, d), 1); v = rnd((L, d), 2)
+    o, lse = fwd(q, k, v, 0.7, causal)
+    for i in range(L):
+        n = i + 1 if causal else L
+        np.testing.assert_allclose(o[i], v[:n].mean(0), atol=1e-13)
+        assert abs(lse[i] - math.log(n)) < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_key_rows(causal):
+    L, d = 29, 16
+    u = rnd((d,), 3)
+    q = rnd((L, d), 4); k = np.tile(u, (L, 1)); v = rnd((L, d), 5)
+    o, lse = fwd(q, k, v, 0.25, causal)
+    for i in range(L):
+        n = i + 1 if causal else L
+        np.testing.assert_allclose(o[i], v[:n].mean(0), atol=1e-13)
+        assert abs(lse[i] - (0.25 * q[i] @ u + math.log(n))) < 1e-12
+
+
+def test_single_dominant_score():
+    L, d = 20, 8
+    q = rnd((L, d), 6); k = rnd((L, d), 7) * 0.01; v = rnd((L, d), 8)
+    i, jstar = 5, 13
+    k[jstar] = 400.0 * q[i] / (q[i] @ q[i])        # s_i,j* = scale * 400 dominates the row
+    o, _ = fwd(q, k, v, 0.5, False)
+    np.testing.assert_allclose(o[i], v[jstar], atol=1e-12)
+
+
+def test_causal_row_zero_is_first_value():
+    L, d = 16, 8
+    q, k, v = rnd((L, d), 9), rnd((L, d), 10), rnd((L, d), 11)
+    o, lse = fwd(q, k, v, 0.3, True)
+    np.testing.assert_allclose(o[0], v[0], atol=0)
+    assert abs(lse[0] - 0.3 * q[0] @ k[0]) < 1e-14
+
+
+# ------------------------------------------------------------- invariants
+
+def test_key_shift_invariance():
+    L, d, s = 24, 8, 0.4
+    q, k, v = rnd((L, d), 12), rnd((L, d), 13), rnd((L, d), 14)
+    u = rnd((d,), 15)
+    o1, l1 = fwd(q, k, v, s, True)
+    o2, l2 = fwd(q, k + u, v, s, True)
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1 + s * q @ u, atol=1e-12)
+
+
+def test_permutations_and_linearity():
+    L, d, s = 19, 8, 0.35
+    q, k, v = rnd((L, d), 16), rnd((L, d), 17), rnd((L, d), 18)
+    o, lse = fwd(q, k, v, s, False)
+    perm = np.random.default_rng(19).permutation(L)
+    o_kv, _ = fwd(q, k[perm], v[perm], s, False)
+    np.testing.assert_allclose(o_kv, o, atol=1e-12)
+    o_q, l_q = fwd(q[perm], k, v, s, False)
+    np.testing.assert_allclose(o_q, o[perm], atol=1e-12)
+    np.testing.assert_allclose(l_q, lse[perm], atol=1e-12)
+    v2 = rnd((L, d), 20)
+    o2, _ = fwd(q, k, v2, s, False)
+    o3, _ = fwd(q, k, 2.0 * v - 3.0 * v2, s, False)
+    np.testing.assert_allclose(o3, 2.0 * o - 3.0 * o2, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_bounds(causal):
+    L, d, s = 33, 16, 0.25
+    q, k, v = rnd((L, d), 21), rnd((L, d), 22) * 3, rnd((L, d), 23)
+    _, lse = fwd(q, k, v, s, causal)
+    S = s * q @ k.T
+    for i in range(L):
+        n = i + 1 if causal else L
+        m = S[i, :n].max()
+        assert m - 1e-12 <= lse[i] <= m + math.log(n) + 1e-12
+
+
+# --------------------------------------------------- library cross-check
+
+def _torch_ref(q, k, v, scale, causal):
+    """torch fp64 SDPA over [B,H,N,d] from [B,N,H,d]."""
+    tq, tk, tv = (torch.tensor(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_sdpa_fp64(causal):
+    B, N, H, d, s = 2, 45, 3, 16, 0.3
+    q, k, v = rnd((B, N, H, d), 24), rnd((B, N, H, d), 25), rnd((B, N, H, d), 26)
+    o, lse = oracle.forward(q.reshape(-1, H, d), k.reshape(-1, H, d), v.reshape(-1, H, d), scale=s,
+                            causal=causal, N=N)
+    ref = _torch_ref(q, k, v, s, causal).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(o.reshape(B, N, H, d), ref, atol=1e-12)
+    # LSE through torch.logsumexp on a masked score matrix
+    S = torch.einsum("bnhd,bmhd->bhnm", torch.tensor(q), torch.tensor(k)) * s
+    if causal:
+        S = S.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    ref_lse = torch.logsumexp(S, -1).permute(0, 2, 1).numpy()
+    np.testing.assert_allclose(lse.reshape(B, N, H), ref_lse, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grads_match_torch_autograd_fp64(causal):
+    B, N, H, d, s = 1, 33, 2, 8, 0.4
+    q, k, v, do = (rnd((B, N, H, d), 30 + t) for t in range(4))
+    dq, dk, dv = oracle.backward(*(x.reshape(-1, H, d) for x in (q, k, v, do)), scale=s, causal=causal, N=N)
+    tq, tk, tv = (torch.tensor(x).permute(0, 2, 1, 3).requires_grad_() for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=s)
+    out.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    for mine, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine.reshape(B, N, H, d), t.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
+# ------------------------------------------------- tiled == definition
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Br,Bc", [(1, 1), (3, 3), (16, 16), (64, 64), (37, 37), (3, 16), (16, 3),
+                                   (64, 5)])
+def test_online_softmax_tiled_equals_definition(causal, Br, Bc):
+    L, d, s = 37, 8, 0.5
+    q, k, v = rnd((L, d), 40), rnd((L, d), 41) * 4.0, rnd((L, d), 42)
+    o, lse = fwd(q, k, v, s, causal)
+    ot, lt = oracle.forward_tiled_head(q, k, v, scale=s, causal=causal, Br=Br, Bc=Bc)
+    np.testing.assert_allclose(ot, o, atol=1e-12)
+    np.testing.assert_allclose(lt, lse, atol=1e-12)
+
+
+def test_online_softmax_tiled_equals_definition_with_dropout():
+    L, d, s = 40, 8, 0.5
+    q, k, v = rnd((L, d), 43), rnd((L, d), 44), rnd((L, d), 45)
+    o, lse = fwd(q, k, v, s, True, dropout_p=0.3, seed=99)
+    ot, lt = oracle.forward_tiled_head(q, k, v, scale=s, causal=True, Br=7, Bc=9, dropout_p=0.3, seed=99)
+    np.testing.assert_allclose(ot, o, atol=1e-12)
+    np.testing.assert_allclose(lt, lse, atol=1e-12)
+
+
+# -------------------------------------------------- finite differences
+
+def _loss(q, k, v, do, s, causal, **kw):
+    o, _ = fwd(q, k, v, s, causal, **kw)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("L,d", [(6, 4), (16, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.4])
+def test_backward_finite_differences(L, d, causal, p):
+    s = 0.6
+    q, k, v, do = (rnd((L, d), 50 + t) for t in range(4))
+    kw = dict(dropout_p=p, seed=1234) if p else {}
+    dq, dk, dv = bwd(q, k, v, do, s, causal, **kw)
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for trial in range(3):
+            delta = rnd((L, d), 100 + 10 * which + trial)
+            args = [q, k, v]
+            plus = [a + h * delta if t == which else a for t, a in enumerate(args)]
+            minus = [a - h * delta if t == which else a for t, a in enumerate(args)]
+            fd = (_loss(*plus, do, s, causal, **kw) - _loss(*minus, do, s, causal, **kw)) / (2 * h)
+            an = float((grad * delta).sum())
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_sum_invariants(causal):
+    L, d = 31, 8
+    q, k, v, do = (rnd((L, d), 60 + t) for t in range(4))
+    dq, dk, dv = bwd(q, k, v, do, 0.3, causal)
+    np.testing.assert_allclose(dk.sum(0), 0.0, atol=1e-12)           # rows of dS sum to zero
+    np.testing.assert_allclose(dv.sum(0), do.sum(0), atol=1e-12)     # columns of P sum ... rows sum to 1
+
+
+# ------------------------------------------------------------- varlen
+
+def test_varlen_equals_separate_sequences():
+    lens = [5, 1, 17, 9]
+    H, d, s = 2, 8, 0.4
+    T = sum(lens)
+    q, k, v, do = (rnd((T, H, d), 70 + t) for t in range(4))
+    o, lse = oracle.forward(q, k, v, scale=s, causal=True, lengths=lens)
+    dq, dk, dv = oracle.backward(q, k, v, do, scale=s, causal=True, lengths=lens)
+    st = 0
+    for L in lens:
+        sl = slice(st, st + L)
+        o1, l1 = oracle.forward(q[sl], k[sl], v[sl], scale=s, causal=True, N=L)
+        g1 = oracle.backward(q[sl], k[sl], v[sl], do[sl], scale=s, causal=True, N=L)
+        np.testing.assert_array_equal(o[sl], o1)
+        np.testing.assert_array_equal(lse[sl], l1)
+        for a, b in zip((dq, dk, dv), g1):
+            np.testing.assert_array_equal(a[sl], b)
+        # and each sequence against torch's SDPA
+        ref = _torch_ref(q[None, sl], k[None, sl], v[None, sl], s, True).permute(0, 2, 1, 3).numpy()[0]
+        np.testing.assert_allclose(o[sl], ref, atol=1e-12)
+        st += L
+
+
+def test_head_selection_computes_only_requested_heads():
+    B, N, H, d = 2, 12, 3, 8
+    q, k, v, do = (rnd((B * N, H, d), 80 + t) for t in range(4))
+    o, lse = oracle.forward(q, k, v, scale=0.3, causal=True, N=N)
+    os_, ls = oracle.forward(q, k, v, scale=0.3, causal=True, N=N, heads=[(1, 2), (0, 1)])
+    for b, h in ((1, 2), (0, 1)):
+        np.testing.assert_array_equal(os_[b * N:(b + 1) * N, h], o[b * N:(b + 1) * N, h])
+        np.testing.assert_array_equal(ls[b * N:(b + 1) * N, h], lse[b * N:(b + 1) * N, h])
+    assert np.isnan(os_[0:N, 0]).all()
+
+
+# -------------------------------------------------------------- dropout
+
+@pytest.fixture(scope="module")
+def rocrand_philox(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path_factory.mktemp("philox") / "philox_rocrand")
+    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-O1", os.path.join(HERE, "helpers", "philox_rocrand.cpp"),
+                           "-o", exe], stderr=subprocess.DEVNULL)
+    return exe
+
+
+def test_philox_matches_rocrand(rocrand_philox):
+    rng = np.random.default_rng(90)
+    # the helper reaches counter word 1 through a 64-bit offset of 4 * block,
+    # so word 1 stays below 2^30 (the attention counter uses col / 4 there)
+    cases = [[0, 0, 0, 0, 0, 0], [1, 2, 3, 4, 5, 6], [0xFFFFFFFF, 2**30 - 1] + [0xFFFFFFFF] * 4]
+    for _ in range(200):
+        c = list(map(int, rng.integers(0, 2**32, 6)))
+        c[1] %= 2**30
+        cases.append(c)
+    inp = "\n".join(" ".join(str(x) for x in c) for c in cases) + "\n"
+    out = subprocess.run([rocrand_philox], input=inp, capture_output=True, text=True, check=True).stdout
+    ref = [list(map(int, line.split())) for line in out.strip().splitlines()]
+    assert len(ref) == len(cases)
+    for c, r in zip(cases, ref):
+        assert oracle.philox4x32_10(c[:4], c[4:]) == r, c
+
+
+def test_keep_mask_uses_documented_counter_layout():
+    seed, p = 0x123456789ABCDEF0, 0.25
+    t = oracle.dropout_threshold(p)
+    m = oracle.keep_mask(seed, p, b=3, h=5, L=13)
+    for i in range(13):
+        for j in range(13):
+            words = oracle.philox4x32_10([i, j // 4, 5, 3], [seed & 0xFFFFFFFF, seed >> 32])
+            assert m[i, j] == (words[j % 4] >= t)
+
+
+def test_keep_threshold_boundary():
+    # an element whose Philox word equals the threshold is kept; one above is dropped
+    seed, b, h, i, j = 42, 1, 2, 3, 6
+    w = oracle.philox4x32_10([i, j // 4, h, b], [seed, 0])[j % 4]
+    assert oracle.keep(seed, w, b, h, i, j)
+    assert not oracle.keep(seed, w + 1, b, h, i, j)
+
+
+def test_keep_rate_statistics():
+    p = 0.1
+    m = oracle.keep_mask(1005, p, b=0, h=0, L=700)
+    n = m.size
+    expect = 1.0 - oracle.dropout_threshold(p) / 2**32
+    sigma = math.sqrt(n * expect * (1 - expect))
+    assert abs(int(m.sum()) - n * expect) < 5 * sigma
+    # different heads / batches give different masks
+    assert (m != oracle.keep_mask(1005, p, b=0, h=1, L=700)).mean() > 0.1
+    assert (m != oracle.keep_mask(1005, p, b=1, h=0, L=700)).mean() > 0.1
+
+
+def test_dropout_forward_matches_masked_torch_reference():
+    L, d, s, p, seed = 23, 8, 0.45, 0.3, 77
+    q, k, v = rnd((L, d), 91), rnd((L, d), 92), rnd((L, d), 93)
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, s, causal, dropout_p=p, seed=seed)
+        o_nd, lse_nd = fwd(q, k, v, s, causal)
+        np.testing.assert_allclose(lse, lse_nd, atol=0)          # LSE excludes dropout
+        S = torch.tensor(q) @ torch.tensor(k).T * s
+        if causal:
+            S = S.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+        P = torch.softmax(S, -1)
+        keep = torch.tensor(oracle.keep_mask(seed, p, 0, 0, L), dtype=torch.float64)
+        ref = (P * keep / (1.0 - float(np.float32(p)))) @ torch.tensor(v)
+        np.testing.assert_allclose(o, ref.numpy(), atol=1e-12)
+
+
+def test_dropout_one_hot_probe_recovers_mask():
+    # Q = K = 0 and one-hot V rows: O[i][c] = keep(i, o + c) / (n_i (1 - p))
+    L, d, p, seed = 24, 8, 0.5, 5
+    q = np.zeros((L, d)); k = np.zeros((L, d))
+    for off in range(0, L, d):
+        v = np.zeros((L, d))
+        for c in range(d):
+            if off + c < L:
+                v[off + c, c] = 1.0
+        o, _ = fwd(q, k, v, 1.0, True, dropout_p=p, seed=seed)
+        mask = oracle.keep_mask(seed, p, 0, 0, L)
+        for i in range(L):
+            for c in range(d):
+                j = off + c
+                want = mask[i, j] / ((i + 1) * (1 - p)) if j <= i else 0.0
+                assert abs(o[i, c] - want) < 1e-14
+
+
+def test_tiny_dropout_probability_equals_no_dropout():
+    L, d = 20, 8
+    q, k, v = rnd((L, d), 94), rnd((L, d), 95), rnd((L, d), 96)
+    assert oracle.dropout_threshold(1e-12) == 0          # every element kept
+    o1, _ = fwd(q, k, v, 0.5, True, dropout_p=1e-12, seed=3)
+    o2, _ = fwd(q, k, v, 0.5, True)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
