@@ -1,0 +1,163 @@
+"""ctypes marshalling for libfa.so (see include/fa.h for the contract).
+
+Tensors are torch tensors on the GPU; torch only provides device memory and
+the current stream.  Shapes: fixed length q, k, v are [B, N, H, d] (any
+token stride, unit stride inside a token, e.g. views into a packed
+[B, N, 3, H, d] tensor); varlen q, k, v are [total, H, d] with int32
+cu_seqlens on the device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_DTYPE_F16 = 0
+FA_DTYPE_BF16 = 1
+_DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fa error {code}: {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m exact_tiled_attention_40_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, i64, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_uint64
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64]
+    lib.fa_forward.restype = i
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64,
+                                vp, ctypes.c_size_t]
+    lib.fa_backward.restype = i
+    lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_backward_workspace_size.restype = ctypes.c_size_t
+    lib.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
+    lib.fa_dropout_mask.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def fa_strerror(code: int) -> str:
+    return _lib.fa_strerror(int(code)).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise FAError(code, fa_strerror(code))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _geometry(q, cu_seqlens, max_seqlen):
+    """(B, N, H, d, ld) of a q/k/v tensor."""
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("fixed-length q/k/v must be [B, N, H, d]")
+        B, N, H, d = q.shape
+        if q.stride(3) != 1 or q.stride(2) != d:
+            raise ValueError("head dim and heads must be contiguous inside a token")
+        if q.stride(0) != N * q.stride(1):
+            raise ValueError("tokens of consecutive batches must be evenly spaced")
+        return B, N, H, d, q.stride(1)
+    if q.dim() != 3:
+        raise ValueError("varlen q/k/v must be [total, H, d]")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be an int32 device tensor")
+    if max_seqlen is None:
+        raise ValueError("varlen needs max_seqlen")
+    _, H, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("head dim and heads must be contiguous inside a token")
+    return cu_seqlens.numel() - 1, int(max_seqlen), H, d, q.stride(0)
+
+
+def _same_geometry(ref, *ts):
+    for t in ts:
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and dq, dk, dv) must share shape, strides, dtype and device")
+
+
+def fa_forward(q, k, v, *, scale=None, causal=False, cu_seqlens=None, max_seqlen=None, dropout_p=0.0, seed=0,
+               out=None, lse=None, stream=None):
+    """Returns (o, lse).  o is contiguous with q's logical shape; lse is float32
+    [B, N, H] (fixed length) or [total, H] (varlen)."""
+    _same_geometry(q, k, v)
+    if q.dtype not in _DTYPES:
+        raise FAError(3, fa_strerror(3))
+    B, N, H, d, ld = _geometry(q, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check(_lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
+                           int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
+                           _stream(stream), _DTYPES[q.dtype], ld))
+    return out, lse
+
+
+def fa_backward_workspace_size(B: int, N: int, H: int, d: int) -> int:
+    return int(_lib.fa_backward_workspace_size(B, N, H, d))
+
+
+def fa_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=None, max_seqlen=None,
+                dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Returns (dq, dk, dv).  Freshly allocated gradients are contiguous; pass
+    dq/dk/dv views (e.g. into a packed [B, N, 3, H, d] buffer) with q's
+    strides to write in place."""
+    _same_geometry(q, k, v)
+    if q.dtype not in _DTYPES:
+        raise FAError(3, fa_strerror(3))
+    B, N, H, d, ld = _geometry(q, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if not (o.is_contiguous() and dout.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("o, dout and lse must be contiguous")
+    if dq is None and dk is None and dv is None:
+        if ld != H * d:
+            raise ValueError("pass dq/dk/dv explicitly for strided q/k/v")
+        dq, dk, dv = (torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    _same_geometry(q, dq, dk, dv)
+    need = fa_backward_workspace_size(B, N, H, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(_lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                            _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(cu_seqlens),
+                            float(dropout_p), int(seed) & (2**64 - 1), _stream(stream), _DTYPES[q.dtype], ld,
+                            _ptr(workspace), workspace.numel() * workspace.element_size()))
+    return dq, dk, dv
+
+
+def fa_dropout_mask(b: int, h: int, N: int, dropout_p: float, seed: int, *, out=None, device="cuda",
+                    stream=None):
+    """uint8 [N, N] keep mask (1 = kept) of head (b, h) as the kernels draw it."""
+    if out is None:
+        out = torch.empty((N, N), dtype=torch.uint8, device=device)
+    _check(_lib.fa_dropout_mask(_ptr(out), b, h, N, float(dropout_p), int(seed) & (2**64 - 1), _stream(stream)))
+    return out

@@ -1,0 +1,120 @@
+// C-ABI front end of libfa: argument validation (host only, before any HIP
+// call), dtype/shape dispatch and workspace carving.  Every entry point
+// returns an fa_status code; none allocates, synchronizes or aborts.
+#include "../../include/fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared checks of fa_forward / fa_backward; fills the launch description.
+int check_common(int B, int H, int N, int d, float scale, float dropout_p, int dtype, int64_t ld_qkv,
+                 const int32_t* cu_seqlens, int causal, uint64_t seed, fa::AttnShape* s) {
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_BAD_SHAPE;
+  // all token offsets must fit in 32-bit signed ints (B*N tokens) and byte
+  // offsets in 64 bits
+  if ((int64_t)B * N > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_ARGUMENT;
+  if (!(dropout_p >= 0.f) || !(dropout_p < 1.f)) return FA_ERR_BAD_ARGUMENT;
+  const int64_t hd = (int64_t)H * d;
+  const int64_t ld = ld_qkv == 0 ? hd : ld_qkv;
+  if (ld < hd || (ld % 8) != 0) return FA_ERR_ALIGNMENT;
+  if (cu_seqlens && !aligned16(cu_seqlens) && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return FA_ERR_ALIGNMENT;
+  s->B = B;
+  s->H = H;
+  s->N = N;
+  s->d = d;
+  s->ld = ld;
+  s->cu = cu_seqlens;
+  s->causal = causal != 0;
+  s->bf16 = dtype == FA_DTYPE_BF16;
+  s->scale = scale;
+  s->dropout = dropout_p > 0.f;
+  const double t = std::floor((double)dropout_p * 4294967296.0);
+  s->drop_thresh = s->dropout ? (uint32_t)t : 0u;
+  s->drop_rescale = s->dropout ? 1.0f / (1.0f - dropout_p) : 1.0f;
+  s->seed = seed;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+               int dtype, int64_t ld_qkv) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  fa::AttnShape s;
+  const int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
+  if (rc != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGNMENT;
+  const hipError_t e = fa::launch_forward(s, q, k, v, o, lse, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_backward_workspace_size(int B, int N, int H, int d) {
+  if (B < 1 || N < 1 || H < 1 || d < 1) return 0;
+  const uint64_t rows = (uint64_t)B * (uint64_t)N * (uint64_t)H;
+  if (rows > (UINT64_MAX / 8) / (uint64_t)(d + 64)) return 0;
+  // dQ accumulator (fp32, rows x d) followed by D (fp32, rows), each part
+  // rounded up to 256 bytes
+  const uint64_t acc = (rows * (uint64_t)d * 4 + 255) & ~(uint64_t)255;
+  const uint64_t delta = (rows * 4 + 255) & ~(uint64_t)255;
+  return (size_t)(acc + delta);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream, int dtype, int64_t ld_qkv,
+                void* workspace, size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+  fa::AttnShape s;
+  const int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
+  if (rc != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGNMENT;
+  const size_t need = fa_backward_workspace_size(B, N, H, d);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGNMENT;
+  const uint64_t rows = (uint64_t)B * N * H;
+  float* acc = static_cast<float*>(workspace);
+  float* delta = acc + (((rows * (uint64_t)d * 4 + 255) & ~(uint64_t)255) / 4);
+  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, acc, delta,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed, void* stream) {
+  if (!keep) return FA_ERR_NULL_POINTER;
+  if (b < 0 || h < 0 || N < 1 || (int64_t)N * N > ((int64_t)1 << 40)) return FA_ERR_BAD_SHAPE;
+  if (!(dropout_p >= 0.f) || !(dropout_p < 1.f)) return FA_ERR_BAD_ARGUMENT;
+  const uint32_t t = (uint32_t)std::floor((double)dropout_p * 4294967296.0);
+  const hipError_t e = fa::launch_dropout_mask(keep, b, h, N, t, seed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "B, H and N must be >= 1 (and B*N tokens must fit in int32)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim (64 or 128) or dtype (fp16 or bf16)";
+    case FA_ERR_BAD_ARGUMENT: return "scale must be finite and > 0, dropout_p in [0, 1)";
+    case FA_ERR_ALIGNMENT: return "pointers must be 16-byte aligned, ld_qkv a multiple of 8 and >= H*d";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
+    case FA_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown fa status code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, MFMA wrappers, LDS transpose reads, 16-bit packing, wave-half
+// reductions and the Philox-4x32-10 dropout hash.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D += A * B on a 32x32 tile with a K slice of 16 (bf16 or fp16 inputs,
+// fp32 accumulation).  Lane l holds A row l%32, B column l%32, and K
+// elements 8*(l/32) .. 8*(l/32)+7 of each; the accumulator register r of
+// lane l is element (row 8*(r/4) + 4*(l/32) + r%4, column l%32).
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values -> two 16-bit floats (round to nearest even) in one word.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (BF16) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float to_f32(uint16_t x) {
+  if constexpr (BF16) return __builtin_bit_cast(float, (uint32_t)x << 16);
+  else return (float)__builtin_bit_cast(_Float16, x);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// source lane s supplies the address of four consecutive 16-bit elements;
+// destination lane l receives element l%4 of source lanes 4e + l/4 (e = 0..3).
+// Pointed at a row-major [k][n] tile with lane s addressing row k0 + s/4,
+// columns n0 + 4*(s%4) .. +3, lane l gets column n0 + l%16, rows k0 .. k0+3.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b.
+// Written as inline assembly because the compiler's builtin for it returns
+// the first operand for both results.  The s_nop covers the VALU-write ->
+// permlane-read hazard.
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Reductions over lanes l and l ^ 32, result in every lane: swapping x with
+// a copy of itself leaves the low half's values in a and the high half's in b.
+__device__ __forceinline__ float halves_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// multiply-xor round function with a Weyl-sequence key schedule.
+struct Philox4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+}  // namespace fa

@@ -1,0 +1,327 @@
+// Fused exact attention forward for gfx950 (MI355X).
+//
+// One workgroup = one (batch-or-sequence b, head h, block of kBR queries);
+// four waves, each owning 32 consecutive queries.  The kernel walks the key
+// blocks the block needs (all of them, or only those left of the diagonal
+// when causal), which is the tiling of the lab write-up "FlashAttention"
+// (dpshk.com), section 3.1, with QK^T, softmax and PV fused as in the
+// tiemojia.cn article's "kernel fusion" paragraph:
+//   - K and V tiles (kBC keys) are staged HBM -> registers -> LDS, double
+//     buffered: the next tile's global loads are in flight while the current
+//     tile is consumed.
+//   - The wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (Q stays in
+//     registers as the B operand).  In that orientation each lane owns one
+//     query and 16 keys per 32x32 tile, so the row max and row sum are
+//     in-lane reductions plus one v_permlane32_swap.
+//   - Online softmax (section 3.2 of the write-up): running max m and sum l
+//     per query in fp32; the partial output is rescaled by e^{m_old - m_new};
+//     exponentials use exp2 with scale*log2(e) folded in.
+//   - O^T += V^T P^T: the P accumulator registers are already laid out as
+//     the B operand (the key order inside each 16-key MFMA slice is
+//     permuted, and V is read with the same permutation), V^T comes from the
+//     LDS transpose read ds_read_b64_tr_b16.
+//   - Epilogue: O = O / l in fp32, rounded once to bf16/fp16; LSE = m + ln l.
+#include "fa_device.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 32 * kWaves;  // queries per workgroup
+constexpr int kBC = 64;           // keys per tile
+
+template <int D>
+struct FwdTile {
+  static constexpr int kPad = 8;            // 16-byte row padding against LDS bank conflicts
+  static constexpr int kRow = D + kPad;     // 16-bit elements per LDS row
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kLoads = kBC * kChunksPerRow / kThreads;  // 16-byte loads per thread per tensor
+};
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* cu;
+  int64_t ld;
+  int B, H, N, nqb;
+  float scale_log2;
+  uint32_t drop_thresh;
+  float drop_rescale;
+  uint32_t seed_lo, seed_hi;
+};
+
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
+  using T = FwdTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBC * T::kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kBC * T::kRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h2 = lane >> 5;
+  const int l32 = lane & 31;
+
+  // Workgroup -> (b, h, query block).  Heads vary fastest so that, with the
+  // round-robin dispatch over the 8 XCDs, every query block of one head lands
+  // on the same XCD (K/V reuse in its L2) whenever B*H is a multiple of 8.
+  // Causal: the longest query blocks (last rows) are dispatched first.
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int rank = blockIdx.x / BH;
+  const int b = bh / a.H;
+  const int h = bh % a.H;
+  const int qb = CAUSAL ? a.nqb - 1 - rank : rank;
+  int start, L;
+  if (a.cu) {
+    start = a.cu[b];
+    L = a.cu[b + 1] - start;
+  } else {
+    start = b * a.N;
+    L = a.N;
+  }
+  const int q0 = qb * kBR;
+  if (q0 >= L) return;
+
+  const int64_t ld = a.ld;
+  const uint16_t* kbase = a.k + (int64_t)start * ld + (int64_t)h * D;
+  const uint16_t* vbase = a.v + (int64_t)start * ld + (int64_t)h * D;
+  const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+
+  const int qw = q0 + 32 * w;  // first query of this wave
+  const int qi = qw + l32;     // query owned by this lane
+
+  // Q fragment: B operand of S^T = K Q^T (column = query, K slice = head dim).
+  u32x4 qf[D / 16];
+  {
+    const uint16_t* qp = a.q + (int64_t)(start + qi) * ld + (int64_t)h * D + 8 * h2;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = qi < L ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0, 0, 0, 0};
+  }
+
+  u32x4 kreg[T::kLoads], vreg[T::kLoads];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < T::kLoads; ++u) {
+      const int c = tid + kThreads * u;
+      const int row = c / T::kChunksPerRow;
+      const int col = (c % T::kChunksPerRow) * 8;
+      if (j0 + row < L) {
+        kreg[u] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(j0 + row) * ld + col);
+        vreg[u] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(j0 + row) * ld + col);
+      } else {
+        kreg[u] = u32x4{0, 0, 0, 0};
+        vreg[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < T::kLoads; ++u) {
+      const int c = tid + kThreads * u;
+      const int row = c / T::kChunksPerRow;
+      const int col = (c % T::kChunksPerRow) * 8;
+      *reinterpret_cast<u32x4*>(&ks[buf][row * T::kRow + col]) = kreg[u];
+      *reinterpret_cast<u32x4*>(&vs[buf][row * T::kRow + col]) = vreg[u];
+    }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY;  // running max, in units of log2 (scores * scale * log2 e)
+  float l_run = 0.f;        // this lane's share of the running row sum
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int j0 = t * kBC;
+    if (t + 1 < ntiles) gload(j0 + kBC);
+
+    // A wave whose queries all precede the tile has nothing to do in it.
+    const bool active = !CAUSAL || j0 <= qw + 31;
+    if (active) {
+      // ---- S^T = K Q^T for keys j0 .. j0+63 (two 32-key tiles)
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[kt] = f32x16{};
+        const uint16_t* kp = &ks[cur][(kt * 32 + l32) * T::kRow + 8 * h2];
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) sacc[kt] = mfma32<BF16>(lds_read16(kp + 16 * s), qf[s], sacc[kt]);
+      }
+      // ---- mask keys after the query (causal) and beyond the sequence end
+      const bool need_mask = (CAUSAL && j0 + kBC - 1 > qw) || (j0 + kBC > L);
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kj = j0 + kt * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if ((CAUSAL && kj > qi) || kj >= L) sacc[kt][r] = -INFINITY;
+          }
+      }
+      // ---- online softmax
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+      mx = halves_max(mx);
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], a.scale_log2, -m_use));
+          rs += p;
+          sacc[kt][r] = p;
+        }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+      if constexpr (DROPOUT) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
+            const Philox4 rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b,
+                                              a.seed_lo, a.seed_hi);
+            if (rnd.x < a.drop_thresh) sacc[kt][4 * g + 0] = 0.f;
+            if (rnd.y < a.drop_thresh) sacc[kt][4 * g + 1] = 0.f;
+            if (rnd.z < a.drop_thresh) sacc[kt][4 * g + 2] = 0.f;
+            if (rnd.w < a.drop_thresh) sacc[kt][4 * g + 3] = 0.f;
+          }
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+
+      // ---- O^T += V^T P^T, four 16-key slices
+      const int grp = lane >> 4;
+      const int sl = lane & 15;
+      const int c0 = 16 * (grp & 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int kt = m >> 1;
+        const int sub = (m & 1) * 8;
+        const u32x4 pf = {pack2<BF16>(sacc[kt][sub + 0], sacc[kt][sub + 1]),
+                          pack2<BF16>(sacc[kt][sub + 2], sacc[kt][sub + 3]),
+                          pack2<BF16>(sacc[kt][sub + 4], sacc[kt][sub + 5]),
+                          pack2<BF16>(sacc[kt][sub + 6], sacc[kt][sub + 7])};
+        const int row = 16 * m + 4 * h2 + (sl >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int col = dt * 32 + c0 + 4 * (sl & 3);
+          const u32x2 lo = lds_read_tr(&vs[cur][row * T::kRow + col]);
+          const u32x2 hi = lds_read_tr(&vs[cur][(row + 8) * T::kRow + col]);
+          oacc[dt] = mfma32<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, oacc[dt]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.f ? (DROPOUT ? a.drop_rescale : 1.f) / l_tot : 0.f;
+  if (qi < L) {
+    uint16_t* op = a.o + (int64_t)(start + qi) * a.H * D + (int64_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * h2;
+        const u32x2 pk = {pack2<BF16>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv),
+                          pack2<BF16>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + d0) = pk;
+      }
+    if (h2 == 0) a.lse[(int64_t)(start + qi) * a.H + h] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+hipError_t launch_fwd_t(const FwdArgs& args, int nblocks, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT>), dim3(nblocks), dim3(kThreads), 0, stream,
+                     args);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_fwd_d(const AttnShape& s, const FwdArgs& args, int nblocks, hipStream_t stream) {
+  if (s.causal)
+    return s.dropout ? launch_fwd_t<D, BF16, true, true>(args, nblocks, stream)
+                     : launch_fwd_t<D, BF16, true, false>(args, nblocks, stream);
+  return s.dropout ? launch_fwd_t<D, BF16, false, true>(args, nblocks, stream)
+                   : launch_fwd_t<D, BF16, false, false>(args, nblocks, stream);
+}
+
+// Dropout keep mask of one head, N x N bytes: one thread per 4 consecutive
+// columns of a row (one Philox block).
+__global__ __launch_bounds__(256) void fa_dropout_mask_kernel(uint8_t* keep, int b, int h, int N,
+                                                              uint32_t thresh, uint32_t seed_lo,
+                                                              uint32_t seed_hi) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int groups = (N + 3) / 4;
+  if (t >= (int64_t)N * groups) return;
+  const int i = (int)(t / groups);
+  const int j4 = (int)(t % groups) * 4;
+  const Philox4 r = philox4x32_10((uint32_t)i, (uint32_t)j4 >> 2, (uint32_t)h, (uint32_t)b, seed_lo, seed_hi);
+  const uint32_t words[4] = {r.x, r.y, r.z, r.w};
+  for (int e = 0; e < 4 && j4 + e < N; ++e) keep[(int64_t)i * N + j4 + e] = words[e] >= thresh ? 1 : 0;
+}
+
+}  // namespace
+
+hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, const void* v, void* o,
+                          float* lse, hipStream_t stream) {
+  FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.cu = s.cu;
+  a.ld = s.ld;
+  a.B = s.B;
+  a.H = s.H;
+  a.N = s.N;
+  a.nqb = (s.N + kBR - 1) / kBR;
+  a.scale_log2 = s.scale * kLog2e;
+  a.drop_thresh = s.drop_thresh;
+  a.drop_rescale = s.drop_rescale;
+  a.seed_lo = (uint32_t)s.seed;
+  a.seed_hi = (uint32_t)(s.seed >> 32);
+  const int64_t nblocks = (int64_t)a.nqb * s.B * s.H;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (s.d == 64)
+    return s.bf16 ? launch_fwd_d<64, true>(s, a, (int)nblocks, stream)
+                  : launch_fwd_d<64, false>(s, a, (int)nblocks, stream);
+  return s.bf16 ? launch_fwd_d<128, true>(s, a, (int)nblocks, stream)
+                : launch_fwd_d<128, false>(s, a, (int)nblocks, stream);
+}
+
+hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,
+                               hipStream_t stream) {
+  const int64_t work = (int64_t)N * ((N + 3) / 4);
+  const int64_t nblocks = (work + 255) / 256;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fa_dropout_mask_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, keep, b, h, N,
+                     thresh, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,33 @@
+// Internal interface between the C-ABI front end (fa_api.cpp) and the
+// kernel launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AttnShape {
+  int B, H, N, d;
+  int64_t ld;              // elements between consecutive tokens of q, k, v, dq, dk, dv
+  const int32_t* cu;       // device prefix sums (varlen) or nullptr
+  bool causal;
+  bool bf16;
+  float scale;
+  bool dropout;
+  uint32_t drop_thresh;    // floor(p * 2^32)
+  float drop_rescale;      // 1 / (1 - p)
+  uint64_t seed;
+};
+
+hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, const void* v, void* o,
+                          float* lse, hipStream_t stream);
+
+hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, float* dq_acc, float* delta, hipStream_t stream);
+
+hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,
+                               hipStream_t stream);
+
+}  // namespace fa

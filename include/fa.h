@@ -1,0 +1,130 @@
+/*
+ * fa.h — C ABI of the exact tiled attention library (libfa.so, gfx950).
+ *
+ * What it computes: exact scaled-dot-product attention in the FlashAttention
+ * style.  The forward pass tiles Q, K and V, forms S = scale * Q K^T one tile
+ * at a time, runs the online softmax (running row max m and row sum l, with
+ * the partial output rescaled by e^{m_old - m_new}) and accumulates P V
+ * without ever writing the N x N matrix; it stores O and the per-row
+ * log-sum-exp.  The backward pass recomputes P from that log-sum-exp instead
+ * of reading a stored P and forms dV, dK and dQ (dQ through an fp32
+ * accumulator).
+ *   - three-step definition S = QK^T, P = softmax(S), O = PV: lab write-up
+ *     "FlashAttention" (dpshk.com), section 2.1;
+ *   - tiling, online softmax and recomputation: the same write-up,
+ *     sections 3.1, 3.2 and 3.3;
+ *   - argument set (q, k, v, dropout_p, softmax_scale, causal), the
+ *     [batch, seq, heads, head_dim] layout, fp16/bf16 only: the write-up's
+ *     section 4.2 and the FlashAttention library overview's usage example;
+ *   - variable-length batches (cu_seqlens): the varlen interface named in
+ *     section 4.2 of the write-up;
+ *   - packed QKV ([B, N, 3, H, d]): the qkvpacked example of the tiemojia.cn
+ *     article, reached here through the row stride ld_qkv.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees, synchronizes or aborts.  Work is
+ *     enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and runs asynchronously.
+ *   - Fixed length (cu_seqlens == NULL): q, k, v and their gradients are
+ *     [B, N, H, d] with consecutive tokens ld_qkv elements apart (ld_qkv == 0
+ *     means H*d, i.e. contiguous; packed QKV passes 3*H*d).  o and dout are
+ *     always contiguous [B, N, H, d].  lse is float32 [B, N, H].
+ *   - Varlen (cu_seqlens != NULL): cu_seqlens is a DEVICE int32 array of
+ *     B + 1 prefix sums (cu_seqlens[0] = 0, non-decreasing); sequence b holds
+ *     tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of [total, H, d] tensors, and
+ *     lse is [total, H].  N must be >= every sequence length (it sizes the
+ *     grid).  Causal masking and dropout indices are local to each sequence;
+ *     queries never see another sequence.  Its contents are a precondition
+ *     the library does not read on the host.
+ *   - Causal: query i sees keys j <= i (queries and keys have equal length).
+ *   - scale multiplies Q K^T before the softmax (1/sqrt(d) is the usual value).
+ *   - Dropout (0 < dropout_p < 1) drops entries of the normalised P before
+ *     the P V product and scales kept entries by 1/(1 - dropout_p); the
+ *     log-sum-exp excludes dropout.  Element (b, h, i, j) is kept iff word
+ *     j mod 4 of Philox-4x32-10 with key (seed low 32 bits, seed high 32
+ *     bits) and counter (i, j / 4, h, b) is >= floor(dropout_p * 2^32)
+ *     (Salmon et al., SC'11).  Forward and backward must get the same seed and
+ *     dropout_p.  dropout_p == 0 runs the no-dropout kernels.
+ *   - dtype is FA_DTYPE_F16 or FA_DTYPE_BF16 for every tensor except lse and
+ *     the workspace (float32).  d must be 64 or 128.
+ *   - Pointers must be 16-byte aligned and ld_qkv a multiple of 8.
+ *   - Outputs must not alias inputs; dq, dk and dv may point into one packed
+ *     [B, N, 3, H, d] buffer when ld_qkv = 3*H*d.
+ *   - Every argument is checked on the host before any HIP call; a failed
+ *     check returns a nonzero FA_ERR_* code and enqueues nothing.  A launch
+ *     error returns FA_ERR_HIP.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
+    FA_ERR_BAD_SHAPE = 2,      /* B, H or N < 1, or a size overflows */
+    FA_ERR_UNSUPPORTED = 3,    /* d not in {64, 128} or unknown dtype */
+    FA_ERR_BAD_ARGUMENT = 4,   /* scale not finite, dropout_p not in [0, 1) */
+    FA_ERR_ALIGNMENT = 5,      /* pointer not 16-byte aligned or bad ld_qkv */
+    FA_ERR_WORKSPACE = 6,      /* workspace NULL or smaller than required */
+    FA_ERR_HIP = 7             /* a HIP launch reported an error */
+};
+
+/* Forward pass.
+ *   q, k, v : input, layout above, row stride ld_qkv.
+ *   o       : output, contiguous [tokens, H, d], dtype.
+ *   lse     : output, float32 [tokens, H]: natural-log log-sum-exp of the
+ *             scaled scores of each query row over its visible keys.
+ * Lab write-up sections 3.1-3.2 (tiling + online softmax); library overview
+ * usage example (flash_attn_func arguments). */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+               int dtype, int64_t ld_qkv);
+
+/* Bytes of device workspace fa_backward needs for B sequences of at most N
+ * tokens with H heads of size d: an fp32 dQ accumulator [B*N, H, d] and the
+ * fp32 row terms D = rowsum(dO * O) [B*N, H].  Returns 0 if the size
+ * overflows.  Host-only, never fails otherwise. */
+size_t fa_backward_workspace_size(int B, int N, int H, int d);
+
+/* Backward pass (recomputation from lse, lab write-up section 3.3).
+ *   q, k, v, o, lse : what fa_forward was given / produced.
+ *   dout            : contiguous [tokens, H, d] gradient of the loss wrt o.
+ *   dq, dk, dv      : outputs, row stride ld_qkv.
+ *   workspace       : device memory of at least fa_backward_workspace_size
+ *                     bytes, 16-byte aligned; no initialisation needed; its
+ *                     contents are overwritten.
+ * Enqueues: a preprocess kernel (D = rowsum(dO * O), zero the dQ
+ * accumulator), the main kernel (one workgroup per key block), and a
+ * conversion kernel (dQ accumulator -> dtype). */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes);
+
+/* Dropout keep mask of a single (b, h) head as the fused kernels draw it:
+ * keep[i * N + j] = 1 if element (i, j) is kept, 0 if dropped, for
+ * 0 <= i, j < N (both local indices; causal masking is NOT applied).  keep
+ * is a device buffer of N*N bytes.  Exposes the kernels' hash so that tests
+ * can compare it bit for bit with an independent implementation. */
+int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed,
+                    void* stream);
+
+/* Static description of an error code (never NULL). */
+const char* fa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,126 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library validates every argument on the host before its first HIP call,
+so each error code can be forced here without a device.  Valid calls are
+never made on the CPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "exact_tiled_attention_40_amd", "libfa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libfa.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_backward", "fa_backward_workspace_size", "fa_dropout_mask", "fa_forward",
+                                    "fa_strerror"]
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        getattr(lib, name)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(LIB)
+    vp, i, f, i64, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_uint64
+    L.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64]
+    L.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64, vp,
+                              ctypes.c_size_t]
+    L.fa_backward_workspace_size.argtypes = [i, i, i, i]
+    L.fa_backward_workspace_size.restype = ctypes.c_size_t
+    L.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
+    L.fa_strerror.argtypes = [i]
+    L.fa_strerror.restype = ctypes.c_char_p
+    return L
+
+
+P = 0x10000  # a fake, 16-byte aligned "device" address: never dereferenced on error paths
+
+FWD_OK = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=128, d=64, scale=0.125, causal=0, cu=None, p=0.0,
+              seed=0, stream=None, dtype=1, ld=0)
+
+
+def fwd(lib, **over):
+    a = dict(FWD_OK, **over)
+    return lib.fa_forward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                          a["causal"], a["cu"], a["p"], a["seed"], a["stream"], a["dtype"], a["ld"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=70000, N=70000), 2),
+    (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3), (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=0.0), 4), (dict(scale=-1.0), 4),
+    (dict(p=1.0), 4), (dict(p=-0.1), 4), (dict(p=float("nan")), 4),
+    (dict(ld=100), 5), (dict(ld=127), 5), (dict(q=P + 8), 5), (dict(o=P + 2), 5), (dict(lse=P + 4), 5),
+])
+def test_forward_rejects_bad_arguments(lib, over, code):
+    assert fwd(lib, **over) == code
+
+
+def test_backward_checks(lib):
+    need = lib.fa_backward_workspace_size(1, 128, 2, 64)
+    assert need >= 128 * 2 * 64 * 4 + 128 * 2 * 4
+
+    def bwd(ws=P, nbytes=None, **over):
+        a = dict(FWD_OK, **over)
+        return lib.fa_backward(a["q"], a["k"], a["v"], a["o"], a["lse"], P, P, P, P, a["B"], a["H"], a["N"], a["d"],
+                               a["scale"], a["causal"], a["cu"], a["p"], a["seed"], None, a["dtype"], a["ld"], ws,
+                               need if nbytes is None else nbytes)
+    assert bwd(ws=None) == 6
+    assert bwd(nbytes=need - 1) == 6
+    assert bwd(ws=P + 4) == 5
+    assert bwd(d=80) == 3
+    assert bwd(q=None) == 1
+    assert bwd(scale=0.0) == 4
+
+
+def test_workspace_size_edge_cases(lib):
+    assert lib.fa_backward_workspace_size(0, 1, 1, 64) == 0
+    assert lib.fa_backward_workspace_size(1, 1, 1, 64) > 0
+    assert lib.fa_backward_workspace_size(2**31 - 1, 2**31 - 1, 2**31 - 1, 128) == 0   # overflow
+
+
+def test_dropout_mask_checks(lib):
+    assert lib.fa_dropout_mask(None, 0, 0, 8, 0.1, 1, None) == 1
+    assert lib.fa_dropout_mask(P, 0, 0, 0, 0.1, 1, None) == 2
+    assert lib.fa_dropout_mask(P, -1, 0, 8, 0.1, 1, None) == 2
+    assert lib.fa_dropout_mask(P, 0, 0, 8, 1.5, 1, None) == 4
+
+
+def test_strerror_covers_every_code(lib):
+    msgs = [lib.fa_strerror(c).decode() for c in range(8)]
+    assert len(set(msgs)) == 8
+    assert lib.fa_strerror(99).decode().startswith("unknown")
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    # the Python binding has no fallback: with libfa.so missing, import raises
+    import shutil
+    import sys
+    pkg = tmp_path / "exact_tiled_attention_40_amd"
+    shutil.copytree(os.path.join(ROOT, "exact_tiled_attention_40_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    code = "import exact_tiled_attention_40_amd"
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "libfa.so is missing" in r.stderr
