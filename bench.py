@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Attention forward + backward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+fa_forward (fused tiled forward) followed by the three backward kernels
+(preprocess, main, dQ conversion), with every input resident in HBM.  The
+default workload is the causal B=4, H=8, N=4096, d=128 bf16 configuration.
+W untimed steps run first, then exactly K timed steps bracketed by device
+synchronisation; HIP events on the library's stream time each kernel of every
+step.  Rank 0 prints one JSON line.
+
+Work convention: a visible (query, key) pair costs 4*d flops forward and
+10*d flops backward (B*H*N(N+1)/2 pairs causal, B*H*N^2 otherwise); masked
+work inside diagonal tiles is not counted.  Peak = MI355X dense bf16/fp16
+MFMA, 2.5 PFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (% of MFMA bf16 peak), B4 H8 N4096 d128 causal"
+PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = {
+    "fa_fwd_kernel": ["fa_fwd.hip", "fa_device.hpp"],
+    "fa_bwd_main_kernel": ["fa_bwd.hip", "fa_device.hpp"],
+}
+
+
+def visible_pairs(wl, lengths=None) -> int:
+    lens = lengths if lengths is not None else [wl.N] * wl.B
+    if wl.causal:
+        return wl.H * sum(L * (L + 1) // 2 for L in lens)
+    return wl.H * sum(L * L for L in lens)
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_tiled_attention_40_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def cpu_baseline(wl, x, n_heads: int):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload:
+    n_heads (batch, head) pairs at full sequence length, forward + backward."""
+    import numpy as np
+    import oracle
+    from workloads import as_f64_tokens
+    oracle.build()
+    nseq = wl.B
+    pairs = [(0, 0), (nseq - 1, wl.H - 1), (nseq // 2, wl.H // 2), (0, wl.H - 1)][:max(1, n_heads)]
+    sel = []
+    for s, h in pairs:
+        rows = slice(s * wl.N, (s + 1) * wl.N)
+        sel.append([as_f64_tokens(t)[rows, h:h + 1] for t in (x.q, x.k, x.v, x.do)])
+    t0 = time.perf_counter()
+    for q, k, v, do in sel:
+        oracle.forward(q, k, v, scale=wl.scale, causal=wl.causal, N=wl.N)
+        oracle.backward(q, k, v, do, scale=wl.scale, causal=wl.causal, N=wl.N)
+    dt = time.perf_counter() - t0
+    per_head = (wl.N * (wl.N + 1) // 2) if wl.causal else wl.N * wl.N
+    flops = 14.0 * wl.d * per_head * len(sel)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{len(sel)} of {wl.B * wl.H} (batch, head) pairs of the {wl.name} workload at full "
+                      f"length, fp64 forward + backward, {flops / 1e9:.1f} GFLOP"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload index (3 = the causal headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels shard by (batch, head) "
+              f"and need no collective, so there is no multi-GPU run to time.", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_tiled_attention_40_amd as fa
+    import workloads
+
+    wl = workloads.CONFIGS[args.config]
+    if wl.varlen:
+        print("bench.py times the fixed-length workloads", file=sys.stderr)
+        return 2
+    x = workloads.make_inputs(wl)
+    dev = torch.device("cuda")
+    if x.qkv is not None:
+        qkv = x.qkv.to(dev)
+        q, k, v = qkv.unbind(2)
+        dqkv = torch.empty_like(qkv)
+        dq, dk, dv = dqkv.unbind(2)
+    else:
+        q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    do = x.do.to(dev)
+    o = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_backward_workspace_size(wl.B, wl.N, wl.H, wl.d), dtype=torch.uint8, device=dev)
+    kw = dict(scale=wl.scale, causal=wl.causal, dropout_p=wl.dropout_p, seed=wl.seed)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        fa.fa_forward(q, k, v, out=o, lse=lse, stream=stream, **kw)
+        if ev: ev[1].record(stream)
+        for s in range(3):
+            fa.fa_backward_stage(s, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream, **kw)
+            if ev: ev[2 + s].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["fa_fwd_kernel", "fa_bwd_pre_kernel", "fa_bwd_main_kernel", "fa_bwd_dq_kernel"]
+    ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
+    step_ms = events[0][0].elapsed_time(events[-1][4]) / args.steps
+
+    pairs = visible_pairs(wl)
+    fwd_flops = 4.0 * wl.d * pairs
+    bwd_flops = 10.0 * wl.d * pairs
+    total_tflops = (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
+    fwd_tflops = fwd_flops / (ms["fa_fwd_kernel"] * 1e-3) / 1e12
+    bwd_ms = ms["fa_bwd_pre_kernel"] + ms["fa_bwd_main_kernel"] + ms["fa_bwd_dq_kernel"]
+    bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+
+    dom = max(("fa_fwd_kernel", "fa_bwd_main_kernel"), key=lambda n: ms[n])
+    dom_flops = fwd_flops if dom == "fa_fwd_kernel" else bwd_flops
+    achieved = dom_flops / (ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_TFLOPS, "traffic": measured_traffic(dom),
+                "avg_launch_ms": ms[dom], "algorithmic_flops_per_launch": dom_flops}
+
+    elem = 2
+    tokens = wl.B * wl.N
+    helper_bytes = {
+        # algorithmic HBM bytes of the two HBM-bound helpers
+        "fa_bwd_pre_kernel": tokens * wl.H * (2 * wl.d * elem + 4 + wl.d * 4),
+        "fa_bwd_dq_kernel": tokens * wl.H * (wl.d * 4 + wl.d * elem),
+    }
+    line = {
+        "metric": METRIC,
+        "value": total_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
+                   "dropout_p": wl.dropout_p, "packed_qkv": wl.packed},
+        "frac_of_peak": total_tflops / PEAK_TFLOPS,
+        "fwd": {"tflops": fwd_tflops, "ms": ms["fa_fwd_kernel"], "frac": fwd_tflops / PEAK_TFLOPS},
+        "bwd": {"tflops": bwd_tflops, "ms": bwd_ms, "frac": bwd_tflops / PEAK_TFLOPS},
+        "kernel_ms": ms,
+        "helper_gbs": {n: b / (ms[n] * 1e-3) / 1e9 for n, b in helper_bytes.items()},
+        "wall_s_timed": wall,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

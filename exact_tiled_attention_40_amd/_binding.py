@@ -34,7 +34,7 @@ def library_path() -> str:
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m exact_tiled_attention_40_amd.build`")
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_tiled_attention_40_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, f, i64, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_uint64
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64]
@@ -42,6 +42,8 @@ def _load():
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64,
                                 vp, ctypes.c_size_t]
     lib.fa_backward.restype = i
+    lib.fa_backward_stage.argtypes = [i] + lib.fa_backward.argtypes
+    lib.fa_backward_stage.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
     lib.fa_backward_workspace_size.restype = ctypes.c_size_t
     lib.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
@@ -131,6 +133,25 @@ def fa_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=N
     """Returns (dq, dk, dv).  Freshly allocated gradients are contiguous; pass
     dq/dk/dv views (e.g. into a packed [B, N, 3, H, d] buffer) with q's
     strides to write in place."""
+    return _backward(None, q, k, v, o, lse, dout, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
+                     max_seqlen=max_seqlen, dropout_p=dropout_p, seed=seed, dq=dq, dk=dk, dv=dv,
+                     workspace=workspace, stream=stream)
+
+
+def fa_backward_stage(stage, q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=None,
+                      max_seqlen=None, dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None,
+                      stream=None):
+    """One backward stage (0 preprocess, 1 main, 2 dQ conversion); the caller
+    passes the same dq/dk/dv and workspace to all three."""
+    if dq is None or dk is None or dv is None or workspace is None:
+        raise ValueError("fa_backward_stage needs explicit dq, dk, dv and workspace")
+    return _backward(int(stage), q, k, v, o, lse, dout, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
+                     max_seqlen=max_seqlen, dropout_p=dropout_p, seed=seed, dq=dq, dk=dk, dv=dv,
+                     workspace=workspace, stream=stream)
+
+
+def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_seqlen, dropout_p, seed, dq, dk,
+              dv, workspace, stream):
     _same_geometry(q, k, v)
     if q.dtype not in _DTYPES:
         raise FAError(3, fa_strerror(3))
@@ -147,10 +168,13 @@ def fa_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=N
     need = fa_backward_workspace_size(B, N, H, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(_lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                            _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(cu_seqlens),
-                            float(dropout_p), int(seed) & (2**64 - 1), _stream(stream), _DTYPES[q.dtype], ld,
-                            _ptr(workspace), workspace.numel() * workspace.element_size()))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+            float(scale), int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
+            _stream(stream), _DTYPES[q.dtype], ld, _ptr(workspace), workspace.numel() * workspace.element_size())
+    if stage is None:
+        _check(_lib.fa_backward(*args))
+    else:
+        _check(_lib.fa_backward_stage(stage, *args))
     return dq, dk, dv
 
 

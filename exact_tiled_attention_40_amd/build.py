@@ -1,6 +1,6 @@
 """Build libfa.so (the gfx950 HIP kernels + C-ABI front end) in-tree.
 
-    python -m exact_tiled_attention_40_amd.build
+    python exact_tiled_attention_40_amd/build.py
 
 Each source is compiled with hipcc for gfx950 only, then linked into
 ``exact_tiled_attention_40_amd/libfa.so``.  Packed-fp32 VALU instructions

@@ -72,10 +72,10 @@ size_t fa_backward_workspace_size(int B, int N, int H, int d) {
   return (size_t)(acc + delta);
 }
 
-int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream, int dtype, int64_t ld_qkv,
-                void* workspace, size_t workspace_bytes) {
+static int backward_impl(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                         int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                         int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
   fa::AttnShape s;
   const int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
@@ -89,9 +89,26 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
   const uint64_t rows = (uint64_t)B * N * H;
   float* acc = static_cast<float*>(workspace);
   float* delta = acc + (((rows * (uint64_t)d * 4 + 255) & ~(uint64_t)255) / 4);
-  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, acc, delta,
+  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, acc, delta, stages,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream, int dtype, int64_t ld_qkv,
+                void* workspace, size_t workspace_bytes) {
+  return backward_impl(fa::kBwdAll, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes);
+}
+
+int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                      int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                      int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes) {
+  if (stage < 0 || stage > 2) return FA_ERR_BAD_ARGUMENT;
+  return backward_impl(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes);
 }
 
 int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed, void* stream) {

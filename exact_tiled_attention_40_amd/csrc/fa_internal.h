@@ -25,7 +25,10 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
 
 hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, float* dq_acc, float* delta, hipStream_t stream);
+                           void* dv, float* dq_acc, float* delta, int stages, hipStream_t stream);
+
+// Stage bits of launch_backward.
+constexpr int kBwdPre = 1, kBwdMain = 2, kBwdDq = 4, kBwdAll = 7;
 
 hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,
                                hipStream_t stream);

@@ -112,6 +112,19 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
                 int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes);
 
+/* One of the three kernels fa_backward enqueues, for callers that time or
+ * schedule them separately: stage 0 = preprocess (D = rowsum(dO * O) into
+ * the workspace, zero the dQ accumulator), 1 = main kernel (dK, dV and the
+ * dQ accumulator), 2 = dQ conversion.  Stages 0, 1, 2 enqueued in this order
+ * on one stream with identical arguments do exactly what fa_backward does;
+ * each stage reads the workspace the previous one wrote.  Arguments and
+ * errors as fa_backward; a stage outside 0..2 returns FA_ERR_BAD_ARGUMENT. */
+int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, float scale, int causal,
+                      const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                      int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes);
+
 /* Dropout keep mask of a single (b, h) head as the fused kernels draw it:
  * keep[i * N + j] = 1 if element (i, j) is kept, 0 if dropped, for
  * 0 <= i, j < N (both local indices; causal masking is NOT applied).  keep

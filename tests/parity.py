@@ -87,16 +87,24 @@ def compare_forward(x: Inputs, o_gpu, lse_gpu, pairs, o_ref, lse_ref):
     return eo, el
 
 
-def rel_fro(x: Inputs, g_gpu, g_ref, pairs):
+def rel_fro(x: Inputs, g_gpu, g_ref, pairs, floor_ref=None):
+    """||G - G*||_F / ||G*||_F over the given heads (and the worst single head).
+
+    A gradient can vanish exactly (dQ and dK when a row sees a single key);
+    then the denominator is floored at ||floor_ref||_F (the dV reference, the
+    scale of the gradients), so rounding noise is judged against that scale."""
     g = tokens_f64(g_gpu)
-    num = den = 0.0
+    num = den = fden = 0.0
     worst = 0.0
     for s, h in pairs:
         r = token_rows(x, s)
         a, b = g[r, h], g_ref[r, h]
         n, d = float(((a - b) ** 2).sum()), float((b ** 2).sum())
+        f = float((floor_ref[r, h] ** 2).sum()) if floor_ref is not None else 0.0
         num += n
         den += d
-        if d > 0:
-            worst = max(worst, (n / d) ** 0.5)
+        fden += f
+        if max(d, f) > 0:
+            worst = max(worst, (n / max(d, f)) ** 0.5)
+    den = max(den, fden)
     return (num / den) ** 0.5 if den > 0 else (0.0 if num == 0 else float("inf")), worst

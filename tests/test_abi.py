@@ -25,8 +25,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_backward", "fa_backward_workspace_size", "fa_dropout_mask", "fa_forward",
-                                    "fa_strerror"]
+    assert declared_functions() == ["fa_backward", "fa_backward_stage", "fa_backward_workspace_size",
+                                    "fa_dropout_mask", "fa_forward", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -46,6 +46,7 @@ def lib():
     L.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64]
     L.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64, vp,
                               ctypes.c_size_t]
+    L.fa_backward_stage.argtypes = [i] + L.fa_backward.argtypes
     L.fa_backward_workspace_size.argtypes = [i, i, i, i]
     L.fa_backward_workspace_size.restype = ctypes.c_size_t
     L.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
@@ -93,6 +94,12 @@ def test_backward_checks(lib):
     assert bwd(d=80) == 3
     assert bwd(q=None) == 1
     assert bwd(scale=0.0) == 4
+    a = dict(FWD_OK)
+    for stage in (-1, 3):
+        assert lib.fa_backward_stage(stage, P, P, P, P, P, P, P, P, P, 1, 2, 128, 64, 0.125, 0, None, 0.0, 0, None, 1,
+                                     0, P, need) == 4
+    assert lib.fa_backward_stage(1, P, P, P, P, P, P, P, P, P, 1, 2, 128, 96, 0.125, 0, None, 0.0, 0, None, 1, 0,
+                                 P, need) == 3
 
 
 def test_workspace_size_edge_cases(lib):
