@@ -70,28 +70,39 @@ def measured_traffic(kernel: str):
 
 def cpu_baseline(wl, x, n_heads: int):
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    n_heads (batch, head) pairs at full sequence length, forward + backward."""
-    import numpy as np
+    n_heads (batch, head) pairs at full sequence length (0 = every pair),
+    forward + backward, OpenMP over the pairs on all host cores."""
     import oracle
     from workloads import as_f64_tokens
     oracle.build()
-    nseq = wl.B
-    pairs = [(0, 0), (nseq - 1, wl.H - 1), (nseq // 2, wl.H // 2), (0, wl.H - 1)][:max(1, n_heads)]
-    sel = []
-    for s, h in pairs:
-        rows = slice(s * wl.N, (s + 1) * wl.N)
-        sel.append([as_f64_tokens(t)[rows, h:h + 1] for t in (x.q, x.k, x.v, x.do)])
+    all_pairs = [(s, h) for s in range(wl.B) for h in range(wl.H)]
+    sel = all_pairs if n_heads <= 0 or n_heads >= len(all_pairs) else all_pairs[::len(all_pairs) // n_heads][:n_heads]
+    q, k, v, do = (as_f64_tokens(t) for t in (x.q, x.k, x.v, x.do))
     t0 = time.perf_counter()
-    for q, k, v, do in sel:
-        oracle.forward(q, k, v, scale=wl.scale, causal=wl.causal, N=wl.N)
-        oracle.backward(q, k, v, do, scale=wl.scale, causal=wl.causal, N=wl.N)
+    oracle.forward(q, k, v, scale=wl.scale, causal=wl.causal, N=wl.N, heads=sel)
+    oracle.backward(q, k, v, do, scale=wl.scale, causal=wl.causal, N=wl.N, heads=sel)
     dt = time.perf_counter() - t0
     per_head = (wl.N * (wl.N + 1) // 2) if wl.causal else wl.N * wl.N
     flops = 14.0 * wl.d * per_head * len(sel)
+    what = "all" if len(sel) == len(all_pairs) else f"{len(sel)} of"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
             "seconds": dt,
-            "sample": f"{len(sel)} of {wl.B * wl.H} (batch, head) pairs of the {wl.name} workload at full "
-                      f"length, fp64 forward + backward, {flops / 1e9:.1f} GFLOP"}
+            "sample": f"{what} {len(all_pairs)} (batch, head) pairs of the {wl.name} workload at full length, "
+                      f"fp64 forward + backward, {flops / 1e9:.1f} GFLOP"}
+
+
+def copy_calibration(nbytes: int, steps: int) -> int:
+    """A plain device copy of nbytes, run `steps` times: the reference kernel
+    that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": steps}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -101,12 +112,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index (3 = the causal headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample size in (batch, head) pairs; 0 = all")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="run only the copy-kernel counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels shard by (batch, head) "
               f"and need no collective, so there is no multi-GPU run to time.", file=sys.stderr)
         return 2
+
+    if args.copy_bytes:
+        return copy_calibration(args.copy_bytes, args.steps)
 
     import torch
     import exact_tiled_attention_40_amd as fa

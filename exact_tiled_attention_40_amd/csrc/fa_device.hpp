@@ -67,6 +67,40 @@ __device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Buffer resource over `bytes` bytes from `base`: raw buffer loads at
+// offsets at or past `bytes` return zeros (the hardware range check), which is
+// how ragged tails are zero-filled without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte buffer load of every lane straight into LDS: lane l's 16 bytes land
+// at lds_base + 16*l (lds_base must be wave-uniform).  Issued from inline
+// assembly so that the compiler does not wait for it before unrelated LDS
+// reads (it cannot tell the double buffers apart); callers wait with
+// wait_vmem() before a barrier.  M0 (the LDS base register) is restored.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voffset) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voffset), "s"(r)
+      : "memory");
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// direct-to-LDS loads) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b.
 // Written as inline assembly because the compiler's builtin for it returns
 // the first operand for both results.  The s_nop covers the VALU-write ->

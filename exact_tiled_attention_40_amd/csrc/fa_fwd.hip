@@ -31,13 +31,26 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;  // queries per workgroup
 constexpr int kBC = 64;           // keys per tile
+// The partial output is rescaled only when a row max grows by more than this
+// many powers of two; otherwise the stale max stays the reference, so the
+// unnormalised probabilities stay below 2^8 (exact: O and l share the same
+// reference, and O / l is taken once at the end).
+constexpr float kRescaleLog2 = 8.0f;
 
+// K and V tiles live in LDS as kBC rows of D 16-bit elements without padding.
+// The 16-byte chunk c of row r is stored at chunk position c ^ swz(r): the
+// 16 rows read together by a b128 read land in 16 different chunk positions,
+// and the 4 rows read together by a transpose read in 4 different chunk pairs.
 template <int D>
 struct FwdTile {
-  static constexpr int kPad = 8;            // 16-byte row padding against LDS bank conflicts
-  static constexpr int kRow = D + kPad;     // 16-bit elements per LDS row
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kLoads = kBC * kChunksPerRow / kThreads;  // 16-byte loads per thread per tensor
+  static constexpr int kCPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int kTileElems = kBC * D;
+  static constexpr int kLoadsPerWave = kBC * kCPR / 64 / kWaves;  // 1 KB direct-to-LDS loads per wave per tensor
+  __device__ static __forceinline__ int swz(int r) { return ((r & (kCPR / 2 - 1)) << 1) | ((r / (kCPR / 2)) & 1); }
+  // element offset of (row r, element col) in the swizzled tile
+  __device__ static __forceinline__ int at(int r, int col) {
+    return r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
+  }
 };
 
 struct FwdArgs {
@@ -56,14 +69,14 @@ struct FwdArgs {
 };
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdArgs a) {
   using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBC * T::kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kBC * T::kRow];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
 
@@ -89,6 +102,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   if (q0 >= L) return;
 
   const int64_t ld = a.ld;
+  const uint32_t row_bytes = (uint32_t)ld * 2;
   const uint16_t* kbase = a.k + (int64_t)start * ld + (int64_t)h * D;
   const uint16_t* vbase = a.v + (int64_t)start * ld + (int64_t)h * D;
   const int kv_end = CAUSAL ? min(L, q0 + kBR) : L;
@@ -97,68 +111,76 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const int qw = q0 + 32 * w;  // first query of this wave
   const int qi = qw + l32;     // query owned by this lane
 
-  // Q fragment: B operand of S^T = K Q^T (column = query, K slice = head dim).
+  // Q fragment: B operand of S^T = K Q^T (column = query, K slice = head dim);
+  // rows past the end read as zeros.
   u32x4 qf[D / 16];
   {
-    const uint16_t* qp = a.q + (int64_t)(start + qi) * ld + (int64_t)h * D + 8 * h2;
+    // a wave can start past the end of a ragged sequence: then its range is
+    // empty and every load returns zero
+    const int rows = max(0, min(32, L - qw));
+    const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + (int64_t)(start + min(qw, L - 1)) * ld + (int64_t)h * D, bytes);
+    const uint32_t off = (uint32_t)l32 * row_bytes + 16 * h2;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf[s] = qi < L ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < D / 16; ++s) qf[s] = buffer_load16(qr, off + 32 * s);
+    // Consume the fragment here so the compiler's own wait for these loads
+    // happens now and not inside the tile loop (where it would also wait for
+    // the asynchronous K/V tile loads).
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(qf[s]));
   }
 
-  u32x4 kreg[T::kLoads], vreg[T::kLoads];
-  auto gload = [&](int j0) {
+  // Direct HBM -> LDS tile load: wave w issues kLoadsPerWave 1 KB loads per
+  // tensor; lane l of load u fills chunk position p = (u*kWaves + w)*64 + l.
+  auto issue_tile = [&](int j0, int buf) {
+    const int rows = min(kBC, L - j0);
+    const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
 #pragma unroll
-    for (int u = 0; u < T::kLoads; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c / T::kChunksPerRow;
-      const int col = (c % T::kChunksPerRow) * 8;
-      if (j0 + row < L) {
-        kreg[u] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(j0 + row) * ld + col);
-        vreg[u] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(j0 + row) * ld + col);
-      } else {
-        kreg[u] = u32x4{0, 0, 0, 0};
-        vreg[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < T::kLoads; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c / T::kChunksPerRow;
-      const int col = (c % T::kChunksPerRow) * 8;
-      *reinterpret_cast<u32x4*>(&ks[buf][row * T::kRow + col]) = kreg[u];
-      *reinterpret_cast<u32x4*>(&vs[buf][row * T::kRow + col]) = vreg[u];
+    for (int u = 0; u < T::kLoadsPerWave; ++u) {
+      const int seg = u * kWaves + w;
+      const int p = seg * 64 + lane;
+      const int r = p / T::kCPR;
+      const int c = (p % T::kCPR) ^ T::swz(r);
+      const uint32_t off = (uint32_t)r * row_bytes + 16 * c;
+      buffer_load_lds16(kr, &ks[buf][seg * 512], off);
+      buffer_load_lds16(vr, &vs[buf][seg * 512], off);
     }
   };
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;  // running max, in units of log2 (scores * scale * log2 e)
-  float l_run = 0.f;        // this lane's share of the running row sum
+  float m_run = -INFINITY;  // reference max, in units of log2 (scores * scale * log2 e)
+  float l_run = 0.f;        // this lane's share of the row sum
 
-  gload(0);
-  sstore(0);
+  issue_tile(0, 0);
+  wait_vmem();
   __syncthreads();
+
+  const int grp = lane >> 4;
+  const int sl = lane & 15;
+  const int c0 = 16 * (grp & 1);
 
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     const int j0 = t * kBC;
-    if (t + 1 < ntiles) gload(j0 + kBC);
+    if (t + 1 < ntiles) issue_tile(j0 + kBC, cur ^ 1);
 
     // A wave whose queries all precede the tile has nothing to do in it.
     const bool active = !CAUSAL || j0 <= qw + 31;
     if (active) {
+      const uint16_t* kt_s = ks[cur];
+      const uint16_t* vt_s = vs[cur];
       // ---- S^T = K Q^T for keys j0 .. j0+63 (two 32-key tiles)
       f32x16 sacc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         sacc[kt] = f32x16{};
-        const uint16_t* kp = &ks[cur][(kt * 32 + l32) * T::kRow + 8 * h2];
+        const int r = kt * 32 + l32;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) sacc[kt] = mfma32<BF16>(lds_read16(kp + 16 * s), qf[s], sacc[kt]);
+        for (int s = 0; s < D / 16; ++s) sacc[kt] = mfma32<BF16>(lds_read16(kt_s + T::at(r, 16 * s + 8 * h2)), qf[s], sacc[kt]);
       }
       // ---- mask keys after the query (causal) and beyond the sequence end
       const bool need_mask = (CAUSAL && j0 + kBC - 1 > qw) || (j0 + kBC > L);
@@ -171,16 +193,22 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
             if ((CAUSAL && kj > qi) || kj >= L) sacc[kt][r] = -INFINITY;
           }
       }
-      // ---- online softmax
+      // ---- online softmax with a lazily rescaled reference max
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      mx = halves_max(mx) * a.scale_log2;
+      const bool grow = mx > m_run + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+        m_run = grow ? mx : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -190,8 +218,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
           rs += p;
           sacc[kt][r] = p;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      l_run += rs;
       if constexpr (DROPOUT) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -206,13 +233,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
             if (rnd.w < a.drop_thresh) sacc[kt][4 * g + 3] = 0.f;
           }
       }
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
 
       // ---- O^T += V^T P^T, four 16-key slices
-      const int grp = lane >> 4;
-      const int sl = lane & 15;
-      const int c0 = 16 * (grp & 1);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int kt = m >> 1;
@@ -225,13 +247,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const int col = dt * 32 + c0 + 4 * (sl & 3);
-          const u32x2 lo = lds_read_tr(&vs[cur][row * T::kRow + col]);
-          const u32x2 hi = lds_read_tr(&vs[cur][(row + 8) * T::kRow + col]);
+          const u32x2 lo = lds_read_tr(vt_s + T::at(row, col));
+          const u32x2 hi = lds_read_tr(vt_s + T::at(row + 8, col));
           oacc[dt] = mfma32<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, oacc[dt]);
         }
       }
     }
-    if (t + 1 < ntiles) sstore(cur ^ 1);
+    // the next tile's direct loads (issued above) must have landed, and every
+    // wave must be done with the current buffers, before the next iteration
+    wait_vmem();
     __syncthreads();
   }
 
