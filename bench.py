@@ -112,7 +112,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index (3 = the causal headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample size in (batch, head) pairs; 0 = all")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="oracle sample size in (batch, head) pairs (about 10-30 s of host work); 0 = all")
     ap.add_argument("--copy-bytes", type=int, default=0, help="run only the copy-kernel counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
