@@ -4,8 +4,9 @@
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-fa_forward (fused tiled forward) followed by the three backward kernels
-(preprocess, main, dQ conversion), with every input resident in HBM.  The
+fa_forward (fused tiled forward) followed by the two backward kernels
+(query side: D and dQ; key side: dK and dV), with every input resident in
+HBM.  The
 default workload is the causal B=4, H=8, N=4096, d=128 bf16 configuration.
 W untimed steps run first, then exactly K timed steps bracketed by device
 synchronisation; HIP events on the library's stream time each kernel of every
@@ -36,7 +37,8 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = {
     "fa_fwd_kernel": ["fa_fwd.hip", "fa_device.hpp"],
-    "fa_bwd_main_kernel": ["fa_bwd.hip", "fa_device.hpp"],
+    "fa_bwd_dq_kernel": ["fa_bwd.hip", "fa_device.hpp"],
+    "fa_bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.hpp"],
 }
 
 
@@ -153,46 +155,48 @@ def main() -> int:
         if ev: ev[0].record(stream)
         fa.fa_forward(q, k, v, out=o, lse=lse, stream=stream, **kw)
         if ev: ev[1].record(stream)
-        for s in range(3):
+        for s in range(2):
             fa.fa_backward_stage(s, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream, **kw)
             if ev: ev[2 + s].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    names = ["fa_fwd_kernel", "fa_bwd_pre_kernel", "fa_bwd_main_kernel", "fa_bwd_dq_kernel"]
+    names = ["fa_fwd_kernel", "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"]
     ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
-    step_ms = events[0][0].elapsed_time(events[-1][4]) / args.steps
+    step_ms = events[0][0].elapsed_time(events[-1][3]) / args.steps
 
     pairs = visible_pairs(wl)
     fwd_flops = 4.0 * wl.d * pairs
     bwd_flops = 10.0 * wl.d * pairs
     total_tflops = (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
     fwd_tflops = fwd_flops / (ms["fa_fwd_kernel"] * 1e-3) / 1e12
-    bwd_ms = ms["fa_bwd_pre_kernel"] + ms["fa_bwd_main_kernel"] + ms["fa_bwd_dq_kernel"]
+    bwd_ms = ms["fa_bwd_dq_kernel"] + ms["fa_bwd_dkdv_kernel"]
     bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
 
-    dom = max(("fa_fwd_kernel", "fa_bwd_main_kernel"), key=lambda n: ms[n])
-    dom_flops = fwd_flops if dom == "fa_fwd_kernel" else bwd_flops
-    achieved = dom_flops / (ms[dom] * 1e-3) / 1e12
+    # Algorithmic flops per launch: the forward's 4*d per visible pair; the
+    # backward's 10*d per pair splits into S, dP, dV, dK (8*d, key-side
+    # kernel) and dQ (2*d, query-side kernel, whose S and dP recomputation is
+    # not counted).  Matrix-core work actually issued is 4*d, 6*d and 8*d.
+    algo_flops = {"fa_fwd_kernel": fwd_flops, "fa_bwd_dq_kernel": 2.0 * wl.d * pairs,
+                  "fa_bwd_dkdv_kernel": 8.0 * wl.d * pairs}
+    issued_flops = {"fa_fwd_kernel": fwd_flops, "fa_bwd_dq_kernel": 6.0 * wl.d * pairs,
+                    "fa_bwd_dkdv_kernel": 8.0 * wl.d * pairs}
+    dom = max(names, key=lambda n: ms[n])
+    achieved = algo_flops[dom] / (ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_TFLOPS, "traffic": measured_traffic(dom),
-                "avg_launch_ms": ms[dom], "algorithmic_flops_per_launch": dom_flops}
+                "avg_launch_ms": ms[dom], "algorithmic_flops_per_launch": algo_flops[dom]}
+    per_kernel = {n: {"ms": ms[n], "algorithmic_tflops": algo_flops[n] / (ms[n] * 1e-3) / 1e12,
+                      "issued_mfma_tflops": issued_flops[n] / (ms[n] * 1e-3) / 1e12} for n in names}
 
-    elem = 2
-    tokens = wl.B * wl.N
-    helper_bytes = {
-        # algorithmic HBM bytes of the two HBM-bound helpers
-        "fa_bwd_pre_kernel": tokens * wl.H * (2 * wl.d * elem + 4 + wl.d * 4),
-        "fa_bwd_dq_kernel": tokens * wl.H * (wl.d * 4 + wl.d * elem),
-    }
     line = {
         "metric": METRIC,
         "value": total_tflops,
@@ -211,8 +215,7 @@ def main() -> int:
         "frac_of_peak": total_tflops / PEAK_TFLOPS,
         "fwd": {"tflops": fwd_tflops, "ms": ms["fa_fwd_kernel"], "frac": fwd_tflops / PEAK_TFLOPS},
         "bwd": {"tflops": bwd_tflops, "ms": bwd_ms, "frac": bwd_tflops / PEAK_TFLOPS},
-        "kernel_ms": ms,
-        "helper_gbs": {n: b / (ms[n] * 1e-3) / 1e9 for n, b in helper_bytes.items()},
+        "kernels": per_kernel,
         "wall_s_timed": wall,
         "roofline": roofline,
         "cpu_baseline": None,

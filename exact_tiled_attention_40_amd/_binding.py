@@ -141,8 +141,8 @@ def fa_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=N
 def fa_backward_stage(stage, q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=None,
                       max_seqlen=None, dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None,
                       stream=None):
-    """One backward stage (0 preprocess, 1 main, 2 dQ conversion); the caller
-    passes the same dq/dk/dv and workspace to all three."""
+    """One backward stage (0: D and dQ, 1: dK and dV); the caller passes the
+    same dq/dk/dv and workspace to both, stage 0 first."""
     if dq is None or dk is None or dv is None or workspace is None:
         raise ValueError("fa_backward_stage needs explicit dq, dk, dv and workspace")
     return _backward(int(stage), q, k, v, o, lse, dout, scale=scale, causal=causal, cu_seqlens=cu_seqlens,

@@ -64,12 +64,9 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_backward_workspace_size(int B, int N, int H, int d) {
   if (B < 1 || N < 1 || H < 1 || d < 1) return 0;
   const uint64_t rows = (uint64_t)B * (uint64_t)N * (uint64_t)H;
-  if (rows > (UINT64_MAX / 8) / (uint64_t)(d + 64)) return 0;
-  // dQ accumulator (fp32, rows x d) followed by D (fp32, rows), each part
-  // rounded up to 256 bytes
-  const uint64_t acc = (rows * (uint64_t)d * 4 + 255) & ~(uint64_t)255;
-  const uint64_t delta = (rows * 4 + 255) & ~(uint64_t)255;
-  return (size_t)(acc + delta);
+  if (rows > (UINT64_MAX - 255) / 4) return 0;
+  // D = rowsum(dO * O): fp32 [B*N, H], rounded up to 256 bytes
+  return (size_t)((rows * 4 + 255) & ~(uint64_t)255);
 }
 
 static int backward_impl(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -86,10 +83,8 @@ static int backward_impl(int stages, const void* q, const void* k, const void* v
   const size_t need = fa_backward_workspace_size(B, N, H, d);
   if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGNMENT;
-  const uint64_t rows = (uint64_t)B * N * H;
-  float* acc = static_cast<float*>(workspace);
-  float* delta = acc + (((rows * (uint64_t)d * 4 + 255) & ~(uint64_t)255) / 4);
-  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, acc, delta, stages,
+  float* delta = static_cast<float*>(workspace);
+  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, delta, stages,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -106,7 +101,7 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
                       int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes) {
-  if (stage < 0 || stage > 2) return FA_ERR_BAD_ARGUMENT;
+  if (stage < 0 || stage > 1) return FA_ERR_BAD_ARGUMENT;
   return backward_impl(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
                        dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes);
 }

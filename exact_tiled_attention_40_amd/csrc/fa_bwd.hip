@@ -1,26 +1,38 @@
 // Exact attention backward for gfx950 (MI355X), recomputing P from the
 // saved log-sum-exp instead of reading a stored P (lab write-up
-// "FlashAttention" (dpshk.com), section 3.3).  Three kernels on one stream:
+// "FlashAttention" (dpshk.com), section 3.3).  Two kernels on one stream;
+// neither uses atomics:
 //
-//   fa_bwd_pre   D[t][h] = sum_c dO[t][h][c] * O[t][h][c] (fp32) and zero the
-//                fp32 dQ accumulator rows.  HBM-bound.
-//   fa_bwd_main  one workgroup per (b, h, block of 128 keys); wave w owns
-//                keys 32w .. 32w+31 with K and V of those keys in registers.
-//                For every block of 64 queries that can see the keys:
-//                  S  = Q K^T                 (MFMA, Q from LDS)
-//                  P  = exp(S*scale - LSE)    (causal mask -> 0)
-//                  dP = dO V^T                (MFMA, dO from LDS)
-//                  dS = P * (dP - D)          (dropout: dP scaled by keep/(1-p))
-//                  dV += Z^T dO, dK += dS^T Q (MFMA; Z^T and dS^T straight from
-//                                              the accumulator registers, dO
-//                                              and Q through LDS transpose reads)
-//                  dQacc += dS K              (dS staged in LDS, fp32 atomics)
-//   fa_bwd_dq    dQ = scale * dQacc -> bf16/fp16.
+//   fa_bwd_dq_kernel    one workgroup per (b, h, block of 128 queries), four
+//                       waves of 32 queries.  Prologue: D = rowsum(dO * O)
+//                       for its rows (kept in registers and written to the
+//                       workspace).  For every 64-key tile the queries can
+//                       see (K and V tiles double-buffered HBM -> LDS):
+//                         S^T  = K Q^T              (MFMA, Q in registers)
+//                         dP^T = V dO^T             (MFMA, dO in registers)
+//                         P    = exp(S*scale - LSE)  (masked -> 0)
+//                         dS   = P * (dP - D)        (dropout: dP * keep/(1-p))
+//                         dQ^T += K^T dS^T           (MFMA, fp32 accumulator in
+//                                                     registers, K^T through the
+//                                                     LDS transpose read)
+//                       Epilogue: dQ = scale * dQ, rounded once.
+//   fa_bwd_dkdv_kernel  one workgroup per (b, h, block of 128 keys), four
+//                       waves of 32 keys whose K and V stay in registers.
+//                       For every 64-query tile that can see the keys (Q, dO,
+//                       LSE and D tiles double-buffered HBM -> LDS):
+//                         S  = Q K^T, dP = dO V^T   (MFMA, Q and dO from LDS)
+//                         P, Z = P * keep/(1-p), dS = P * (dP - D)
+//                         dV += Z^T dO, dK += dS^T Q (MFMA; Z^T and dS^T straight
+//                                                    from the accumulator
+//                                                    registers, dO and Q through
+//                                                    the LDS transpose read)
+//                       Epilogue: dK = scale * dK; dK, dV rounded once.
 //
-// The accumulator layout of S = Q K^T puts one key per lane and runs of four
-// consecutive queries in registers, which is exactly the A-operand layout of
-// the dV and dK products once the query order inside each 16-query MFMA
-// slice is permuted (dO and Q are read with the same permutation).
+// Both kernels recompute S and dP (two extra products per visible pair) so
+// that dQ, dK and dV each have one owner: an fp32 atomic reduction of dQ over
+// key blocks would move more bytes through the atomic units than the rest of
+// the backward moves through HBM, while the recomputation runs on the matrix
+// cores.  The dQ kernel runs first because the dK/dV kernel reads its D.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -29,16 +41,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBKV = 32 * kWaves;  // keys per workgroup
-constexpr int kBQ = 64;            // queries per inner iteration
-
-template <int D>
-struct BwdTile {
-  static constexpr int kRow = D + 8;          // padded LDS row (16-bit elements) of Q, dO, K
-  static constexpr int kDsRow = kBQ + 8;      // padded LDS row of dS^T ([key][query])
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kLoads = kBQ * kChunksPerRow / kThreads;  // 16-byte loads per thread per tensor
-};
+constexpr int kBQ = 32 * kWaves;   // queries per dQ workgroup
+constexpr int kBC = 64;            // keys per tile of the dQ kernel
+constexpr int kBKV = 32 * kWaves;  // keys per dK/dV workgroup
+constexpr int kBR = 64;            // queries per tile of the dK/dV kernel
 
 struct BwdArgs {
   const uint16_t* q;
@@ -50,11 +56,10 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;
   float* delta;
   const int32_t* cu;
   int64_t ld;
-  int B, H, N, nkb;
+  int B, H, N, nqb, nkb;
   float scale;
   float scale_log2;
   uint32_t drop_thresh;
@@ -72,57 +77,220 @@ __device__ __forceinline__ void seq_range(const BwdArgs& a, int b, int& start, i
   }
 }
 
-// ---------------------------------------------------------------- preprocess
-// D/8 lanes per (token, head) row; each lane owns 8 consecutive elements.
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdArgs a) {
-  constexpr int kLanesPerRow = D / 8;
-  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
-  const int total = a.cu ? a.cu[a.B] : a.B * a.N;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  const int c = (threadIdx.x % kLanesPerRow) * 8;
-  const bool valid = row < (int64_t)total * a.H;
-  float s = 0.f;
-  if (valid) {
-    const u32x4 o4 = *reinterpret_cast<const u32x4*>(a.o + row * D + c);
-    const u32x4 g4 = *reinterpret_cast<const u32x4*>(a.dout + row * D + c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s += to_f32<BF16>((uint16_t)(o4[e] & 0xffff)) * to_f32<BF16>((uint16_t)(g4[e] & 0xffff));
-      s += to_f32<BF16>((uint16_t)(o4[e] >> 16)) * to_f32<BF16>((uint16_t)(g4[e] >> 16));
-    }
-    float* acc = a.dq_acc + row * D + c;
-    *reinterpret_cast<f32x4*>(acc) = f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(acc + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kLanesPerRow);
-  if (valid && (threadIdx.x % kLanesPerRow) == 0) a.delta[row] = s;
+// Keep factor of element (query i, key j) of head (b, h): 1/(1-p) if kept,
+// 0 if dropped (Philox word j mod 4 of counter (i, j/4, h, b)).
+__device__ __forceinline__ float keep_factor(const BwdArgs& a, int b, int h, int i, int j) {
+  const Philox4 r = philox4x32_10((uint32_t)i, (uint32_t)j >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
+  const uint32_t w = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
+  return w >= a.drop_thresh ? a.drop_rescale : 0.f;
 }
 
-// ---------------------------------------------------------------- main
+// ---------------------------------------------------------------- dQ (+ D)
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(kThreads) void fa_bwd_main_kernel(BwdArgs a) {
-  using T = BwdTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[kBQ * T::kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t do_s[kBQ * T::kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[kBKV * T::kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_s[kBKV * T::kDsRow];
-  __shared__ __attribute__((aligned(16))) float lse_s[kBQ];
-  __shared__ __attribute__((aligned(16))) float dl_s[kBQ];
+__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+  using T = SwzTile<D, kBC>;
+  constexpr int kLoadsPerWave = T::kLoads / kWaves;
+  __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
   const int grp = lane >> 4;
   const int sl = lane & 15;
   const int c0 = 16 * (grp & 1);
 
-  // Workgroup -> (b, h, key block); heads fastest (one head's blocks share an
-  // XCD when B*H is a multiple of 8).  Causal: the first key blocks see the
-  // most queries and go first.
+  // Workgroup -> (b, h, query block): heads fastest (one head's blocks share
+  // an XCD when B*H is a multiple of 8); causal: longest blocks first.
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int rank = blockIdx.x / BH;
+  const int b = bh / a.H;
+  const int h = bh % a.H;
+  const int qb = CAUSAL ? a.nqb - 1 - rank : rank;
+  int start, L;
+  seq_range(a, b, start, L);
+  const int q0 = qb * kBQ;
+  if (q0 >= L) return;
+
+  const int64_t ld = a.ld;
+  const int64_t hd = (int64_t)a.H * D;  // token stride of o, dout
+  const uint32_t row_bytes = (uint32_t)ld * 2;
+  const uint16_t* kbase = a.k + (int64_t)start * ld + (int64_t)h * D;
+  const uint16_t* vbase = a.v + (int64_t)start * ld + (int64_t)h * D;
+  const int kv_end = CAUSAL ? min(L, q0 + kBQ) : L;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+
+  const int qw = q0 + 32 * w;
+  const int qi = qw + l32;
+
+  // Q and dO fragments (B operands: column = query, K slice = head dim) and
+  // D = rowsum(dO * O) of this lane's query; rows past the end read as zeros.
+  u32x4 qf[D / 16], gf[D / 16];
+  float delta;
+  {
+    const int rows = max(0, min(32, L - qw));
+    const int64_t tok = start + min(qw, L - 1);
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(a.q + tok * ld + (int64_t)h * D, rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u);
+    const uint32_t gbytes = rows > 0 ? (uint32_t)(rows - 1) * (uint32_t)hd * 2 + D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.dout + tok * hd + (int64_t)h * D, gbytes);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.o + tok * hd + (int64_t)h * D, gbytes);
+    const uint32_t offq = (uint32_t)l32 * row_bytes + 16 * h2;
+    const uint32_t offg = (uint32_t)l32 * (uint32_t)hd * 2 + 16 * h2;
+    u32x4 of[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = buffer_load16(qr, offq + 32 * s);
+      gf[s] = buffer_load16(gr, offg + 32 * s);
+      of[s] = buffer_load16(orr, offg + 32 * s);
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += to_f32<BF16>((uint16_t)(gf[s][e] & 0xffff)) * to_f32<BF16>((uint16_t)(of[s][e] & 0xffff));
+        acc += to_f32<BF16>((uint16_t)(gf[s][e] >> 16)) * to_f32<BF16>((uint16_t)(of[s][e] >> 16));
+      }
+    delta = halves_sum(acc);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      asm volatile("" : "+v"(qf[s]));
+      asm volatile("" : "+v"(gf[s]));
+    }
+  }
+  // queries past the end: Q = dO = 0 and LSE = 0 give P = 1, dP = 0, dS = 0
+  const float lse2 = qi < L ? a.lse[(int64_t)(start + qi) * a.H + h] * kLog2e : 0.f;
+  if (qi < L && h2 == 0) a.delta[(int64_t)(start + qi) * a.H + h] = delta;
+
+  auto issue_tile = [&](int j0, int buf) {
+    const int rows = min(kBC, L - j0);
+    const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
+#pragma unroll
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      T::load(kr, ks[buf], row_bytes, u * kWaves + w, lane);
+      T::load(vr, vs[buf], row_bytes, u * kWaves + w, lane);
+    }
+  };
+
+  f32x16 qacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) qacc[dt] = f32x16{};
+
+  issue_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int j0 = t * kBC;
+    if (t + 1 < ntiles) issue_tile(j0 + kBC, cur ^ 1);
+
+    const bool active = !CAUSAL || j0 <= qw + 31;
+    if (active) {
+      const uint16_t* kt_s = ks[cur];
+      const uint16_t* vt_s = vs[cur];
+      // ---- S^T = K Q^T and dP^T = V dO^T for keys j0 .. j0+63
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[kt] = f32x16{};
+        pacc[kt] = f32x16{};
+        const int r = kt * 32 + l32;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          sacc[kt] = mfma32<BF16>(lds_read16(kt_s + T::at(r, 16 * s + 8 * h2)), qf[s], sacc[kt]);
+          pacc[kt] = mfma32<BF16>(lds_read16(vt_s + T::at(r, 16 * s + 8 * h2)), gf[s], pacc[kt]);
+        }
+      }
+      // ---- P and dS; register r of tile kt: key j0 + kt*32 + 8*(r/4) + 4*h2 + r%4
+      const bool need_mask = (CAUSAL && j0 + kBC - 1 > qw) || (j0 + kBC > L);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
+          Philox4 rnd;
+          if constexpr (DROPOUT)
+            rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], a.scale_log2, -lse2));
+            if (need_mask && ((CAUSAL && kj4 + e > qi) || kj4 + e >= L)) p = 0.f;
+            float dp = pacc[kt][r];
+            if constexpr (DROPOUT) {
+              const uint32_t word = e == 0 ? rnd.x : e == 1 ? rnd.y : e == 2 ? rnd.z : rnd.w;
+              dp *= word >= a.drop_thresh ? a.drop_rescale : 0.f;
+            }
+            sacc[kt][r] = p * (dp - delta);
+          }
+        }
+      // ---- dQ^T += K^T dS^T, four 16-key slices
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int kt = m >> 1;
+        const int sub = (m & 1) * 8;
+        const u32x4 sf = {pack2<BF16>(sacc[kt][sub + 0], sacc[kt][sub + 1]),
+                          pack2<BF16>(sacc[kt][sub + 2], sacc[kt][sub + 3]),
+                          pack2<BF16>(sacc[kt][sub + 4], sacc[kt][sub + 5]),
+                          pack2<BF16>(sacc[kt][sub + 6], sacc[kt][sub + 7])};
+        const int row = 16 * m + 4 * h2 + (sl >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int col = dt * 32 + c0 + 4 * (sl & 3);
+          const u32x2 lo = lds_read_tr(kt_s + T::at(row, col));
+          const u32x2 hi = lds_read_tr(kt_s + T::at(row + 8, col));
+          qacc[dt] = mfma32<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf, qacc[dt]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- epilogue: register r of tile dt holds head-dim element
+  // dt*32 + 8*(r/4) + 4*h2 + r%4 of query qi
+  if (qi < L) {
+    uint16_t* dqp = a.dq + (int64_t)(start + qi) * ld + (int64_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * h2;
+        const u32x2 pk = {pack2<BF16>(qacc[dt][4 * g + 0] * a.scale, qacc[dt][4 * g + 1] * a.scale),
+                          pack2<BF16>(qacc[dt][4 * g + 2] * a.scale, qacc[dt][4 * g + 3] * a.scale)};
+        *reinterpret_cast<u32x2*>(dqp + d0) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  using T = SwzTile<D, kBR>;
+  constexpr int kLoadsPerWave = T::kLoads / kWaves;
+  __shared__ __attribute__((aligned(1024))) uint16_t qs[2][T::kElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t gs[2][T::kElems];
+  __shared__ __attribute__((aligned(16))) float ls[2][kBR];
+  __shared__ __attribute__((aligned(16))) float dls[2][kBR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5;
+  const int l32 = lane & 31;
+  const int grp = lane >> 4;
+  const int sl = lane & 15;
+  const int c0 = 16 * (grp & 1);
+
+  // Workgroup -> (b, h, key block): heads fastest; causal: the first key
+  // blocks see the most queries and go first.
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;
@@ -134,34 +302,61 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_main_kernel(BwdArgs a) {
   if (j0 >= L) return;
 
   const int64_t ld = a.ld;
-  const int64_t hoff = (int64_t)h * D;
-  const int kw0 = j0 + 32 * w;   // first key of this wave
-  const int kj = kw0 + l32;      // key owned by this lane
+  const int64_t hd = (int64_t)a.H * D;
+  const uint32_t row_bytes = (uint32_t)ld * 2;
+  const uint32_t grow_bytes = (uint32_t)hd * 2;
+  const int kw0 = j0 + 32 * w;  // first key of this wave
+  const int kj = kw0 + l32;     // key owned by this lane
 
-  // K, V fragments of this lane's key (B operand of Q K^T and dO V^T).
+  // K and V fragments of this lane's key (B operands: column = key, K slice =
+  // head dim); keys past the end read as zeros.
   u32x4 kf[D / 16], vf[D / 16];
   {
-    const uint16_t* kp = a.k + (int64_t)(start + kj) * ld + hoff + 8 * h2;
-    const uint16_t* vp = a.v + (int64_t)(start + kj) * ld + hoff + 8 * h2;
+    const int rows = max(0, min(32, L - kw0));
+    const int64_t tok = start + min(kw0, L - 1);
+    const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.k + tok * ld + (int64_t)h * D, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.v + tok * ld + (int64_t)h * D, bytes);
+    const uint32_t off = (uint32_t)l32 * row_bytes + 16 * h2;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      kf[s] = kj < L ? *reinterpret_cast<const u32x4*>(kp + 16 * s) : u32x4{0, 0, 0, 0};
-      vf[s] = kj < L ? *reinterpret_cast<const u32x4*>(vp + 16 * s) : u32x4{0, 0, 0, 0};
+      kf[s] = buffer_load16(kr, off + 32 * s);
+      vf[s] = buffer_load16(vr, off + 32 * s);
     }
-  }
-  // K block in LDS (B operand of dS K, read transposed).
-  {
-    constexpr int kKLoads = kBKV * T::kChunksPerRow / kThreads;
 #pragma unroll
-    for (int u = 0; u < kKLoads; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c / T::kChunksPerRow;
-      const int col = (c % T::kChunksPerRow) * 8;
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (j0 + row < L) x = *reinterpret_cast<const u32x4*>(a.k + (int64_t)(start + j0 + row) * ld + hoff + col);
-      *reinterpret_cast<u32x4*>(&k_s[row * T::kRow + col]) = x;
+    for (int s = 0; s < D / 16; ++s) {
+      asm volatile("" : "+v"(kf[s]));
+      asm volatile("" : "+v"(vf[s]));
     }
   }
+
+  // Query tiles that can see the keys: all, or (causal) from the tile holding
+  // query j0 on.  Rows past the end of the sequence load as zeros (Q = dO = 0,
+  // LSE = D = 0), which gives P = 1, dP = 0 and dS = 0: no contribution.
+  const int i_begin = CAUSAL ? (j0 / kBR) * kBR : 0;
+  const int ntiles = (L - i_begin + kBR - 1) / kBR;
+  const uint16_t* qbase = a.q + (int64_t)start * ld + (int64_t)h * D;
+  const uint16_t* gbase = a.dout + (int64_t)start * hd + (int64_t)h * D;
+  const float* lbase = a.lse + (int64_t)start * a.H + h;
+  const float* dbase = a.delta + (int64_t)start * a.H + h;
+
+  auto issue_tile = [&](int i0, int buf) {
+    const int rows = min(kBR, L - i0);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qbase + (int64_t)i0 * ld, (uint32_t)(rows - 1) * row_bytes + D * 2);
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(gbase + (int64_t)i0 * hd, (uint32_t)(rows - 1) * grow_bytes + D * 2);
+#pragma unroll
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      T::load(qr, qs[buf], row_bytes, u * kWaves + w, lane);
+      T::load(gr, gs[buf], grow_bytes, u * kWaves + w, lane);
+    }
+    if (w == 0) {
+      const __amdgpu_buffer_rsrc_t lr = make_rsrc(lbase + (int64_t)i0 * a.H, (uint32_t)(rows - 1) * a.H * 4 + 4);
+      buffer_load_lds4(lr, ls[buf], (uint32_t)lane * a.H * 4);
+    } else if (w == 1) {
+      const __amdgpu_buffer_rsrc_t dr = make_rsrc(dbase + (int64_t)i0 * a.H, (uint32_t)(rows - 1) * a.H * 4 + 4);
+      buffer_load_lds4(dr, dls[buf], (uint32_t)lane * a.H * 4);
+    }
+  };
 
   f32x16 dv_acc[D / 32], dk_acc[D / 32];
 #pragma unroll
@@ -170,99 +365,56 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_main_kernel(BwdArgs a) {
     dk_acc[dt] = f32x16{};
   }
 
-  // Query blocks that can see this key block.
-  const int i_begin = CAUSAL ? (j0 / kBQ) * kBQ : 0;
-  const int n_iter = (L - i_begin + kBQ - 1) / kBQ;
+  if (ntiles > 0) issue_tile(i_begin, 0);
+  wait_vmem();
+  __syncthreads();
 
-  u32x4 qreg[T::kLoads], oreg[T::kLoads];
-  float lse_r = 0.f, dl_r = 0.f;
-  auto gload = [&](int i0) {
-#pragma unroll
-    for (int u = 0; u < T::kLoads; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c / T::kChunksPerRow;
-      const int col = (c % T::kChunksPerRow) * 8;
-      if (i0 + row < L) {
-        qreg[u] = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(start + i0 + row) * ld + hoff + col);
-        oreg[u] = *reinterpret_cast<const u32x4*>(a.dout + (int64_t)(start + i0 + row) * a.H * D + hoff + col);
-      } else {
-        qreg[u] = u32x4{0, 0, 0, 0};
-        oreg[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < kBQ) {
-      const int i = i0 + tid;
-      // rows past the end get LSE = +inf so that P = 0 there
-      lse_r = i < L ? a.lse[(int64_t)(start + i) * a.H + h] * kLog2e : INFINITY;
-      dl_r = i < L ? a.delta[(int64_t)(start + i) * a.H + h] : 0.f;
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int u = 0; u < T::kLoads; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c / T::kChunksPerRow;
-      const int col = (c % T::kChunksPerRow) * 8;
-      *reinterpret_cast<u32x4*>(&q_s[row * T::kRow + col]) = qreg[u];
-      *reinterpret_cast<u32x4*>(&do_s[row * T::kRow + col]) = oreg[u];
-    }
-    if (tid < kBQ) {
-      lse_s[tid] = lse_r;
-      dl_s[tid] = dl_r;
-    }
-  };
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int i0 = i_begin + t * kBR;
+    if (t + 1 < ntiles) issue_tile(i0 + kBR, cur ^ 1);
 
-  if (n_iter > 0) gload(i_begin);
-  for (int it = 0; it < n_iter; ++it) {
-    const int i0 = i_begin + it * kBQ;
-    sstore();
-    __syncthreads();
-    if (it + 1 < n_iter) gload(i0 + kBQ);
-
-    const bool active = !CAUSAL || i0 + kBQ - 1 >= kw0;
-    uint16_t* dsw = &ds_s[(32 * w + l32) * T::kDsRow];
+    // a wave whose keys all follow every query of the tile has nothing to do
+    const bool active = !CAUSAL || i0 + kBR - 1 >= kw0;
     if (active) {
-      // ---- S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
+      const uint16_t* qt_s = qs[cur];
+      const uint16_t* gt_s = gs[cur];
+      // ---- S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         sacc[qt] = f32x16{};
         pacc[qt] = f32x16{};
-        const uint16_t* qp = &q_s[(qt * 32 + l32) * T::kRow + 8 * h2];
-        const uint16_t* gp = &do_s[(qt * 32 + l32) * T::kRow + 8 * h2];
+        const int r = qt * 32 + l32;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          sacc[qt] = mfma32<BF16>(lds_read16(qp + 16 * s), kf[s], sacc[qt]);
-          pacc[qt] = mfma32<BF16>(lds_read16(gp + 16 * s), vf[s], pacc[qt]);
+          sacc[qt] = mfma32<BF16>(lds_read16(qt_s + T::at(r, 16 * s + 8 * h2)), kf[s], sacc[qt]);
+          pacc[qt] = mfma32<BF16>(lds_read16(gt_s + T::at(r, 16 * s + 8 * h2)), vf[s], pacc[qt]);
         }
       }
-      // ---- P, dS (register r of tile qt: query qt*32 + 8*(r/4) + 4*h2 + r%4)
+      // ---- P, Z, dS; register r of tile qt: query i0 + qt*32 + 8*(r/4) + 4*h2 + r%4
       const bool need_mask = CAUSAL && i0 < kw0 + 31;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qrow = qt * 32 + 8 * g + 4 * h2;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[qrow]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_s[qrow]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&ls[cur][qrow]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dls[cur][qrow]);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int r = 4 * g + t;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qt][r], a.scale_log2, -l4[t]));
-            if (need_mask && kj > i0 + qrow + t) p = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qt][r], a.scale_log2, -l4[e] * kLog2e));
+            if (need_mask && kj > i0 + qrow + e) p = 0.f;
             float dp = pacc[qt][r];
             float z = p;
             if constexpr (DROPOUT) {
-              const uint32_t qi = (uint32_t)(i0 + qrow + t);
-              const Philox4 rnd = philox4x32_10(qi, (uint32_t)kj >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo,
-                                                a.seed_hi);
-              const uint32_t wsel = (kj & 3) == 0 ? rnd.x : (kj & 3) == 1 ? rnd.y : (kj & 3) == 2 ? rnd.z : rnd.w;
-              const float kf_ = wsel >= a.drop_thresh ? a.drop_rescale : 0.f;
-              dp *= kf_;
-              z = p * kf_;
+              const float kfac = keep_factor(a, b, h, i0 + qrow + e, kj);
+              dp *= kfac;
+              z = p * kfac;
             }
-            sacc[qt][r] = z;                  // Z (= P without dropout) for dV
-            pacc[qt][r] = p * (dp - d4[t]);   // dS
+            sacc[qt][r] = z;                 // Z (= P without dropout)
+            pacc[qt][r] = p * (dp - d4[e]);  // dS
           }
         }
       // ---- dV += Z^T dO, dK += dS^T Q over four 16-query slices
@@ -282,75 +434,28 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const int col = dt * 32 + c0 + 4 * (sl & 3);
-          const u32x2 g0 = lds_read_tr(&do_s[row * T::kRow + col]);
-          const u32x2 g1 = lds_read_tr(&do_s[(row + 8) * T::kRow + col]);
+          const u32x2 g0 = lds_read_tr(gt_s + T::at(row, col));
+          const u32x2 g1 = lds_read_tr(gt_s + T::at(row + 8, col));
           dv_acc[dt] = mfma32<BF16>(zf, u32x4{g0[0], g0[1], g1[0], g1[1]}, dv_acc[dt]);
-          const u32x2 q0 = lds_read_tr(&q_s[row * T::kRow + col]);
-          const u32x2 q1 = lds_read_tr(&q_s[(row + 8) * T::kRow + col]);
-          dk_acc[dt] = mfma32<BF16>(sf, u32x4{q0[0], q0[1], q1[0], q1[1]}, dk_acc[dt]);
-        }
-        // dS^T row of this lane's key: four runs of 4 consecutive queries
-      }
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 pk = {pack2<BF16>(pacc[qt][4 * g + 0], pacc[qt][4 * g + 1]),
-                            pack2<BF16>(pacc[qt][4 * g + 2], pacc[qt][4 * g + 3])};
-          *reinterpret_cast<u32x2*>(dsw + qt * 32 + 8 * g + 4 * h2) = pk;
-        }
-    } else {
-      // keys after every query of the block: dS = 0
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(dsw + qt * 32 + 8 * g + 4 * h2) = u32x2{0, 0};
-    }
-    __syncthreads();
-
-    // ---- dQacc[64 x D] += dS K over the 128 keys; wave w: query tile w&1,
-    // head-dim tiles (w>>1)*NCT .. +NCT-1
-    {
-      constexpr int NCT = D / 64;
-      const int qt = w & 1;
-      f32x16 qacc[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) qacc[ct] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < kBKV / 16; ++kk) {
-        const int krow = 16 * kk + 8 * h2 + (sl >> 2);
-        const u32x2 a0 = lds_read_tr(&ds_s[krow * T::kDsRow + qt * 32 + c0 + 4 * (sl & 3)]);
-        const u32x2 a1 = lds_read_tr(&ds_s[(krow + 4) * T::kDsRow + qt * 32 + c0 + 4 * (sl & 3)]);
-        const u32x4 af = {a0[0], a0[1], a1[0], a1[1]};
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const int col = ((w >> 1) * NCT + ct) * 32 + c0 + 4 * (sl & 3);
-          const u32x2 b0 = lds_read_tr(&k_s[krow * T::kRow + col]);
-          const u32x2 b1 = lds_read_tr(&k_s[(krow + 4) * T::kRow + col]);
-          qacc[ct] = mfma32<BF16>(af, u32x4{b0[0], b0[1], b1[0], b1[1]}, qacc[ct]);
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int c = ((w >> 1) * NCT + ct) * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = i0 + qt * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (i < L) atomicAdd(a.dq_acc + ((int64_t)(start + i) * a.H + h) * D + c, qacc[ct][r]);
+          const u32x2 x0 = lds_read_tr(qt_s + T::at(row, col));
+          const u32x2 x1 = lds_read_tr(qt_s + T::at(row + 8, col));
+          dk_acc[dt] = mfma32<BF16>(sf, u32x4{x0[0], x0[1], x1[0], x1[1]}, dk_acc[dt]);
         }
       }
     }
+    wait_vmem();
     __syncthreads();
   }
 
-  // ---- epilogue: dK = scale * dK_acc, dV; register r: key kw0 + 8*(r/4) + 4*h2 + r%4, lane: column
+  // ---- epilogue: register r of tile dt holds key kw0 + 8*(r/4) + 4*h2 + r%4,
+  // head-dim element dt*32 + l32
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = kw0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
       if (j < L) {
-        const int64_t off = (int64_t)(start + j) * ld + hoff + dt * 32 + l32;
+        const int64_t off = (int64_t)(start + j) * ld + (int64_t)h * D + dt * 32 + l32;
         const uint32_t pk = pack2<BF16>(dk_acc[dt][r] * a.scale, dv_acc[dt][r]);
         a.dk[off] = (uint16_t)(pk & 0xffff);
         a.dv[off] = (uint16_t)(pk >> 16);
@@ -358,53 +463,37 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_main_kernel(BwdArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- dQ convert
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fa_bwd_dq_kernel(BwdArgs a) {
-  const int total = a.cu ? a.cu[a.B] : a.B * a.N;
-  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;  // element index in [tokens, H, D]
-  if (idx >= (int64_t)total * a.H * D) return;
-  const int64_t row = idx / D;          // token * H + head
-  const int c = (int)(idx % D);
-  const int64_t tok = row / a.H;
-  const int hh = (int)(row % a.H);
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(a.dq_acc + idx);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(a.dq_acc + idx + 4);
-  const u32x4 pk = {pack2<BF16>(x0[0] * a.scale, x0[1] * a.scale), pack2<BF16>(x0[2] * a.scale, x0[3] * a.scale),
-                    pack2<BF16>(x1[0] * a.scale, x1[1] * a.scale), pack2<BF16>(x1[2] * a.scale, x1[3] * a.scale)};
-  *reinterpret_cast<u32x4*>(a.dq + tok * a.ld + (int64_t)hh * D + c) = pk;
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+hipError_t launch_bwd_t(const AttnShape& s, const BwdArgs& args, int stages, hipStream_t stream) {
+  if (stages & kBwdDq) {
+    const int64_t nb = (int64_t)args.nqb * s.B * s.H;
+    if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT>), dim3((unsigned)nb), dim3(kThreads), 0, stream,
+                       args);
+  }
+  if (stages & kBwdKV) {
+    const int64_t nb = (int64_t)args.nkb * s.B * s.H;
+    if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, DROPOUT>), dim3((unsigned)nb), dim3(kThreads), 0,
+                       stream, args);
+  }
+  return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_bwd_d(const AttnShape& s, const BwdArgs& args, int stages, hipStream_t stream) {
-  const int64_t rows = (int64_t)s.B * s.N * s.H;
-  if (stages & kBwdPre) {
-    constexpr int kRowsPerBlock = 256 / (D / 8);
-    const int64_t nb = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<D, BF16>), dim3((unsigned)nb), dim3(256), 0, stream, args);
-  }
-  if (stages & kBwdMain) {
-    const int64_t nb = (int64_t)args.nkb * s.B * s.H;
-    if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    auto kern = s.causal ? (s.dropout ? fa_bwd_main_kernel<D, BF16, true, true> : fa_bwd_main_kernel<D, BF16, true, false>)
-                         : (s.dropout ? fa_bwd_main_kernel<D, BF16, false, true>
-                                      : fa_bwd_main_kernel<D, BF16, false, false>);
-    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(kThreads), 0, stream, args);
-  }
-  if (stages & kBwdDq) {
-    const int64_t nb = (rows * D / 8 + 255) / 256;
-    if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16>), dim3((unsigned)nb), dim3(256), 0, stream, args);
-  }
-  return hipGetLastError();
+  if (s.causal)
+    return s.dropout ? launch_bwd_t<D, BF16, true, true>(s, args, stages, stream)
+                     : launch_bwd_t<D, BF16, true, false>(s, args, stages, stream);
+  return s.dropout ? launch_bwd_t<D, BF16, false, true>(s, args, stages, stream)
+                   : launch_bwd_t<D, BF16, false, false>(s, args, stages, stream);
 }
 
 }  // namespace
 
 hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, const void* v, const void* o,
-                           const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dq_acc,
-                           float* delta, int stages, hipStream_t stream) {
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
+                           int stages, hipStream_t stream) {
   BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -415,13 +504,13 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  a.dq_acc = dq_acc;
   a.delta = delta;
   a.cu = s.cu;
   a.ld = s.ld;
   a.B = s.B;
   a.H = s.H;
   a.N = s.N;
+  a.nqb = (s.N + kBQ - 1) / kBQ;
   a.nkb = (s.N + kBKV - 1) / kBKV;
   a.scale = s.scale;
   a.scale_log2 = s.scale * kLog2e;

@@ -37,22 +37,6 @@ constexpr int kBC = 64;           // keys per tile
 // reference, and O / l is taken once at the end).
 constexpr float kRescaleLog2 = 8.0f;
 
-// K and V tiles live in LDS as kBC rows of D 16-bit elements without padding.
-// The 16-byte chunk c of row r is stored at chunk position c ^ swz(r): the
-// 16 rows read together by a b128 read land in 16 different chunk positions,
-// and the 4 rows read together by a transpose read in 4 different chunk pairs.
-template <int D>
-struct FwdTile {
-  static constexpr int kCPR = D / 8;                    // 16-byte chunks per row
-  static constexpr int kTileElems = kBC * D;
-  static constexpr int kLoadsPerWave = kBC * kCPR / 64 / kWaves;  // 1 KB direct-to-LDS loads per wave per tensor
-  __device__ static __forceinline__ int swz(int r) { return ((r & (kCPR / 2 - 1)) << 1) | ((r / (kCPR / 2)) & 1); }
-  // element offset of (row r, element col) in the swizzled tile
-  __device__ static __forceinline__ int at(int r, int col) {
-    return r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
-  }
-};
-
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -70,9 +54,10 @@ struct FwdArgs {
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdArgs a) {
-  using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kTileElems];
+  using T = SwzTile<D, kBC>;
+  constexpr int kLoadsPerWave = T::kLoads / kWaves;  // 1 KB direct-to-LDS loads per wave per tensor
+  __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,22 +115,17 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdArgs a) {
     for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(qf[s]));
   }
 
-  // Direct HBM -> LDS tile load: wave w issues kLoadsPerWave 1 KB loads per
-  // tensor; lane l of load u fills chunk position p = (u*kWaves + w)*64 + l.
+  // Direct HBM -> LDS tile load: wave w issues loads w, w + kWaves, ... of
+  // each tensor's tile.
   auto issue_tile = [&](int j0, int buf) {
     const int rows = min(kBC, L - j0);
     const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
 #pragma unroll
-    for (int u = 0; u < T::kLoadsPerWave; ++u) {
-      const int seg = u * kWaves + w;
-      const int p = seg * 64 + lane;
-      const int r = p / T::kCPR;
-      const int c = (p % T::kCPR) ^ T::swz(r);
-      const uint32_t off = (uint32_t)r * row_bytes + 16 * c;
-      buffer_load_lds16(kr, &ks[buf][seg * 512], off);
-      buffer_load_lds16(vr, &vs[buf][seg * 512], off);
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      T::load(kr, ks[buf], row_bytes, u * kWaves + w, lane);
+      T::load(vr, vs[buf], row_bytes, u * kWaves + w, lane);
     }
   };
 

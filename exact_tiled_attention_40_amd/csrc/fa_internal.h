@@ -25,10 +25,11 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
 
 hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, float* dq_acc, float* delta, int stages, hipStream_t stream);
+                           void* dv, float* delta, int stages, hipStream_t stream);
 
-// Stage bits of launch_backward.
-constexpr int kBwdPre = 1, kBwdMain = 2, kBwdDq = 4, kBwdAll = 7;
+// Stage bits of launch_backward: the dQ kernel (which also writes D) and the
+// dK/dV kernel (which reads D).
+constexpr int kBwdDq = 1, kBwdKV = 2, kBwdAll = 3;
 
 hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,
                                hipStream_t stream);

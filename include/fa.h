@@ -7,8 +7,8 @@
  * the partial output rescaled by e^{m_old - m_new}) and accumulates P V
  * without ever writing the N x N matrix; it stores O and the per-row
  * log-sum-exp.  The backward pass recomputes P from that log-sum-exp instead
- * of reading a stored P and forms dV, dK and dQ (dQ through an fp32
- * accumulator).
+ * of reading a stored P and forms dV, dK and dQ, each accumulated in fp32
+ * by the one workgroup that owns it.
  *   - three-step definition S = QK^T, P = softmax(S), O = PV: lab write-up
  *     "FlashAttention" (dpshk.com), section 2.1;
  *   - tiling, online softmax and recomputation: the same write-up,
@@ -91,9 +91,9 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int dtype, int64_t ld_qkv);
 
 /* Bytes of device workspace fa_backward needs for B sequences of at most N
- * tokens with H heads of size d: an fp32 dQ accumulator [B*N, H, d] and the
- * fp32 row terms D = rowsum(dO * O) [B*N, H].  Returns 0 if the size
- * overflows.  Host-only, never fails otherwise. */
+ * tokens with H heads of size d: the fp32 row terms D = rowsum(dO * O)
+ * [B*N, H].  Returns 0 if the size overflows.  Host-only, never fails
+ * otherwise. */
 size_t fa_backward_workspace_size(int B, int N, int H, int d);
 
 /* Backward pass (recomputation from lse, lab write-up section 3.3).
@@ -103,22 +103,24 @@ size_t fa_backward_workspace_size(int B, int N, int H, int d);
  *   workspace       : device memory of at least fa_backward_workspace_size
  *                     bytes, 16-byte aligned; no initialisation needed; its
  *                     contents are overwritten.
- * Enqueues: a preprocess kernel (D = rowsum(dO * O), zero the dQ
- * accumulator), the main kernel (one workgroup per key block), and a
- * conversion kernel (dQ accumulator -> dtype). */
+ * Enqueues two kernels: the query-side kernel (D = rowsum(dO * O) into the
+ * workspace, then dQ, accumulated in fp32 registers over every key block a
+ * query sees) and the key-side kernel (dK and dV, accumulated in fp32
+ * registers over every query block that sees a key; reads D).  Both
+ * recompute S and P from lse; no atomics are used, so results are
+ * deterministic. */
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
                 const void* dout, void* dq, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal,
                 const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
                 int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes);
 
-/* One of the three kernels fa_backward enqueues, for callers that time or
- * schedule them separately: stage 0 = preprocess (D = rowsum(dO * O) into
- * the workspace, zero the dQ accumulator), 1 = main kernel (dK, dV and the
- * dQ accumulator), 2 = dQ conversion.  Stages 0, 1, 2 enqueued in this order
- * on one stream with identical arguments do exactly what fa_backward does;
- * each stage reads the workspace the previous one wrote.  Arguments and
- * errors as fa_backward; a stage outside 0..2 returns FA_ERR_BAD_ARGUMENT. */
+/* One of the two kernels fa_backward enqueues, for callers that time or
+ * schedule them separately: stage 0 = query-side kernel (D into the
+ * workspace, dQ), 1 = key-side kernel (dK, dV; reads D from the workspace).
+ * Stages 0 then 1 enqueued on one stream with identical arguments do exactly
+ * what fa_backward does.  Arguments and errors as fa_backward; a stage
+ * outside 0..1 returns FA_ERR_BAD_ARGUMENT. */
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       int B, int H, int N, int d, float scale, int causal,

@@ -81,7 +81,7 @@ def test_forward_rejects_bad_arguments(lib, over, code):
 
 def test_backward_checks(lib):
     need = lib.fa_backward_workspace_size(1, 128, 2, 64)
-    assert need >= 128 * 2 * 64 * 4 + 128 * 2 * 4
+    assert need >= 128 * 2 * 4
 
     def bwd(ws=P, nbytes=None, **over):
         a = dict(FWD_OK, **over)
@@ -95,7 +95,7 @@ def test_backward_checks(lib):
     assert bwd(q=None) == 1
     assert bwd(scale=0.0) == 4
     a = dict(FWD_OK)
-    for stage in (-1, 3):
+    for stage in (-1, 2):
         assert lib.fa_backward_stage(stage, P, P, P, P, P, P, P, P, P, 1, 2, 128, 64, 0.125, 0, None, 0.0, 0, None, 1,
                                      0, P, need) == 4
     assert lib.fa_backward_stage(1, P, P, P, P, P, P, P, P, P, 1, 2, 128, 96, 0.125, 0, None, 0.0, 0, None, 1, 0,
