@@ -64,9 +64,10 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_backward_workspace_size(int B, int N, int H, int d) {
   if (B < 1 || N < 1 || H < 1 || d < 1) return 0;
   const uint64_t rows = (uint64_t)B * (uint64_t)N * (uint64_t)H;
-  if (rows > (UINT64_MAX - 255) / 4) return 0;
-  // D = rowsum(dO * O): fp32 [B*N, H], rounded up to 256 bytes
-  return (size_t)((rows * 4 + 255) & ~(uint64_t)255);
+  if (rows > ((UINT64_MAX - 255) / 4) / 2) return 0;
+  // D = rowsum(dO * O) and LSE * log2(e): fp32 [B*N, H] each, each rounded up
+  // to 256 bytes
+  return (size_t)(2 * ((rows * 4 + 255) & ~(uint64_t)255));
 }
 
 static int backward_impl(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -84,7 +85,9 @@ static int backward_impl(int stages, const void* q, const void* k, const void* v
   if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGNMENT;
   float* delta = static_cast<float*>(workspace);
-  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, delta, stages,
+  const uint64_t rows = (uint64_t)B * (uint64_t)N * (uint64_t)H;
+  float* lse2 = delta + ((rows * 4 + 255) & ~(uint64_t)255) / 4;
+  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, delta, lse2, stages,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

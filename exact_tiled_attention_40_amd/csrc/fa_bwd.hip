@@ -33,6 +33,8 @@
 // key blocks would move more bytes through the atomic units than the rest of
 // the backward moves through HBM, while the recomputation runs on the matrix
 // cores.  The dQ kernel runs first because the dK/dV kernel reads its D.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -46,6 +48,9 @@ constexpr int kBC = 64;            // keys per tile of the dQ kernel
 constexpr int kBKV = 32 * kWaves;  // keys per dK/dV workgroup
 constexpr int kBR = 64;            // queries per tile of the dK/dV kernel
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100;
+
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -56,7 +61,8 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;
+  float* delta;   // D = rowsum(dO * O), [tokens, H]
+  float* lse2;    // LSE * log2(e), [tokens, H]
   const int32_t* cu;
   int64_t ld;
   int B, H, N, nqb, nkb;
@@ -164,7 +170,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   }
   // queries past the end: Q = dO = 0 and LSE = 0 give P = 1, dP = 0, dS = 0
   const float lse2 = qi < L ? a.lse[(int64_t)(start + qi) * a.H + h] * kLog2e : 0.f;
-  if (qi < L && h2 == 0) a.delta[(int64_t)(start + qi) * a.H + h] = delta;
+  if (qi < L && h2 == 0) {
+    a.delta[(int64_t)(start + qi) * a.H + h] = delta;
+    a.lse2[(int64_t)(start + qi) * a.H + h] = lse2;
+  }
 
   auto issue_tile = [&](int j0, int buf) {
     const int rows = min(kBC, L - j0);
@@ -271,23 +280,170 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Software pipeline over 32-query halves of the 64-query tiles, one wave per
+// SIMD: while the VALU turns S, dP of one half into Z and dS, the matrix cores
+// already compute S, dP of the next half; then dV, dK take the first half's
+// products.  Q/dO tiles are triple-buffered (t in use, t + 1 read by the
+// look-ahead products, t + 2 landing).
+template <int D, bool BF16>
+struct KVState {
+  u32x4 kf[D / 16], vf[D / 16];  // K, V fragments of this lane's key
+  f32x16 dv[D / 32], dk[D / 32];
+};
+
+// Per-lane LDS read addresses of one tile: operand reads (chunk pairs s even
+// / odd) and transpose reads (rows +0 / +8) of the Q and dO tiles.  They are
+// made opaque to the compiler so that every read of the tile becomes one of
+// these registers plus an immediate offset.
+struct TileAddr {
+  uint32_t q0, q1, g0, g1;
+};
+
+__device__ __forceinline__ TileAddr tile_addr(uint32_t qb, uint32_t gb, uint32_t b0, uint32_t b1) {
+  TileAddr t{qb + b0, qb + b1, gb + b0, gb + b1};
+  asm volatile("" : "+v"(t.q0), "+v"(t.q1), "+v"(t.g0), "+v"(t.g1));
+  return t;
+}
+
+// S = Q K^T and dP = dO V^T for queries 32qt .. 32qt+31 of a tile (pipeline
+// prologue only; the loop computes them inside dkdv_half).
+template <int D, bool BF16>
+__device__ __forceinline__ void dkdv_sdp(const KVState<D, BF16>& st, const TileAddr& op, int qt, f32x16& sacc,
+                                         f32x16& pacc) {
+  using T = MTile<D, kBR>;
+  sacc = f32x16{};
+  pacc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const uint32_t qa = (s & 1) ? op.q1 : op.q0, ga = (s & 1) ? op.g1 : op.g0;
+    sacc = mfma32<BF16>(lds_read16_at(qa + T::opnd_off(qt, s)), st.kf[s], sacc);
+    pacc = mfma32<BF16>(lds_read16_at(ga + T::opnd_off(qt, s)), st.vf[s], pacc);
+  }
+}
+
+// One 32-query half (queries 32qt .. 32qt+31 of the tile at tr) of the
+// pipeline, in a fixed instruction order (sched_barrier fences keep the
+// compiler from regrouping it):
+//   phase 1: the look-ahead products S, dP of half nqt of the tile at nop,
+//            their LDS operands read kPF products ahead, with this half's
+//            P, Z, dS (from sacc, pacc) computed element by element between
+//            them;
+//   phase 2: dV += Z^T dO and dK += dS^T Q for this half, the transpose reads
+//            of each product issued kPF2 products ahead.
+// On return sacc, pacc hold the look-ahead S, dP.  Register r of sacc holds
+// query 32qt + 8*(r/4) + 4*(lane/32) + r%4 of this lane's key; lb, db point at
+// LSE*log2(e) and D of the tile, offset by this lane half's first query.
+template <int D, bool BF16, bool MASK, bool DROPOUT>
+__device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st, f32x16& sacc, f32x16& pacc,
+                                          const TileAddr& nop, int nqt, const TileAddr& tr, int qt, uint32_t lb,
+                                          uint32_t db, int i0, int kj, int h2, int b, int h) {
+  using T = MTile<D, kBR>;
+  constexpr int kNP = D / 8;   // look-ahead products (S and dP, D/16 k-steps each)
+  constexpr int kPF = 4;       // operand reads in flight
+  constexpr int kEPP = 16 / kNP;  // softmax elements per product
+  auto opnd = [&](int i) {
+    const int s = i >> 1;
+    const uint32_t base = (i & 1) ? ((s & 1) ? nop.g1 : nop.g0) : ((s & 1) ? nop.q1 : nop.q0);
+    return lds_read16_at(base + T::opnd_off(nqt, s));
+  };
+
+  // ---- phase 1
+  auto lse_d = [&](int g, f32x4& l, f32x4& d) {
+    l = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(lb + 4 * (qt * 32 + 8 * g));
+    d = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(db + 4 * (qt * 32 + 8 * g));
+  };
+  u32x4 ob[kNP];
+  f32x4 l4, d4, l4n, d4n;
+#pragma unroll
+  for (int i = 0; i < kPF; ++i) ob[i] = opnd(i);
+  lse_d(0, l4, d4);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 ns = f32x16{}, np = f32x16{};
+  uint32_t zpk[8], spk[8];  // packed Z, dS pairs (elements 2k, 2k + 1)
+  float zprev = 0.f, dsprev = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNP; ++i) {
+    const int s = i >> 1;
+    if (i & 1)
+      np = mfma32<BF16>(ob[i], st.vf[s], np);
+    else
+      ns = mfma32<BF16>(ob[i], st.kf[s], ns);
+    if (i + kPF < kNP) ob[i + kPF] = opnd(i + kPF);
+#pragma unroll
+    for (int u = 0; u < kEPP; ++u) {
+      const int r = i * kEPP + u;
+      const int g = r >> 2, e = r & 3;
+      if (e == 0 && g < 3) lse_d(g + 1, l4n, d4n);  // next group's LSE, D, four elements ahead
+      const int qrow = qt * 32 + 8 * g + 4 * h2 + e;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, -l4[e]));
+      if (MASK && kj > i0 + qrow) p = 0.f;
+      float dp = pacc[r];
+      float zz = p;
+      if constexpr (DROPOUT) {
+        const float kfac = keep_factor(a, b, h, i0 + qrow, kj);
+        dp *= kfac;
+        zz = p * kfac;
+      }
+      const float dsv = p * (dp - d4[e]);
+      if (r & 1) {
+        zpk[r >> 1] = pack2<BF16>(zprev, zz);
+        spk[r >> 1] = pack2<BF16>(dsprev, dsv);
+      } else {
+        zprev = zz;
+        dsprev = dsv;
+      }
+      if (e == 3) {
+        l4 = l4n;
+        d4 = d4n;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sacc = ns;
+  pacc = np;
+  const u32x4 zf[2] = {u32x4{zpk[0], zpk[1], zpk[2], zpk[3]}, u32x4{zpk[4], zpk[5], zpk[6], zpk[7]}};
+  const u32x4 sf[2] = {u32x4{spk[0], spk[1], spk[2], spk[3]}, u32x4{spk[4], spk[5], spk[6], spk[7]}};
+
+  // ---- phase 2: product j = (slice mm, head-dim tile dt, dV or dK)
+  constexpr int kNA = 2 * 2 * (D / 32);
+  constexpr int kPF2 = 4;
+  auto tr_pair = [&](int j) {
+    const int mm = j / (2 * (D / 32)), dt = (j >> 1) % (D / 32);
+    const uint32_t o = T::tr_off(2 * qt + mm, dt);
+    const uint32_t b0 = (j & 1) ? tr.q0 : tr.g0, b1 = (j & 1) ? tr.q1 : tr.g1;
+    const u32x2 x0 = lds_read_tr_at(b0 + o), x1 = lds_read_tr_at(b1 + o);
+    return u32x4{x0[0], x0[1], x1[0], x1[1]};
+  };
+  u32x4 tb[kNA];
+#pragma unroll
+  for (int j = 0; j < kPF2; ++j) tb[j] = tr_pair(j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < kNA; ++j) {
+    const int mm = j / (2 * (D / 32)), dt = (j >> 1) % (D / 32);
+    if (j & 1)
+      st.dk[dt] = mfma32<BF16>(sf[mm], tb[j], st.dk[dt]);
+    else
+      st.dv[dt] = mfma32<BF16>(zf[mm], tb[j], st.dv[dt]);
+    if (j + kPF2 < kNA) tb[j + kPF2] = tr_pair(j + kPF2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
-  using T = SwzTile<D, kBR>;
-  constexpr int kLoadsPerWave = T::kLoads / kWaves;
-  __shared__ __attribute__((aligned(1024))) uint16_t qs[2][T::kElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t gs[2][T::kElems];
-  __shared__ __attribute__((aligned(16))) float ls[2][kBR];
-  __shared__ __attribute__((aligned(16))) float dls[2][kBR];
+  using T = MTile<D, kBR>;
+  constexpr int kNB = 3;  // Q/dO/LSE/D tile buffers
+  __shared__ __attribute__((aligned(1024))) uint16_t qs[kNB][T::kElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t gs[kNB][T::kElems];
+  __shared__ __attribute__((aligned(16))) float ls[kNB][kBR];
+  __shared__ __attribute__((aligned(16))) float dls[kNB][kBR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
-  const int grp = lane >> 4;
-  const int sl = lane & 15;
-  const int c0 = 16 * (grp & 1);
 
   // Workgroup -> (b, h, key block): heads fastest; causal: the first key
   // blocks see the most queries and go first.
@@ -308,10 +464,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int kw0 = j0 + 32 * w;  // first key of this wave
   const int kj = kw0 + l32;     // key owned by this lane
 
-  // K and V fragments of this lane's key (B operands: column = key, K slice =
-  // head dim); keys past the end read as zeros.
-  u32x4 kf[D / 16], vf[D / 16];
+  KVState<D, BF16> st;
   {
+    // keys past the end read as zeros
     const int rows = max(0, min(32, L - kw0));
     const int64_t tok = start + min(kw0, L - 1);
     const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u;
@@ -320,13 +475,22 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const uint32_t off = (uint32_t)l32 * row_bytes + 16 * h2;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      kf[s] = buffer_load16(kr, off + 32 * s);
-      vf[s] = buffer_load16(vr, off + 32 * s);
+      st.kf[s] = buffer_load16(kr, off + 32 * s);
+      st.vf[s] = buffer_load16(vr, off + 32 * s);
     }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      asm volatile("" : "+v"(kf[s]));
-      asm volatile("" : "+v"(vf[s]));
+      asm volatile("" : "+v"(st.kf[s]));
+      asm volatile("" : "+v"(st.vf[s]));
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      st.dv[dt] = f32x16{};
+      st.dk[dt] = f32x16{};
+      // the accumulators live in AGPRs for the whole loop (only the matrix
+      // cores touch them until the epilogue)
+      asm volatile("" : "+a"(st.dv[dt]));
+      asm volatile("" : "+a"(st.dk[dt]));
     }
   }
 
@@ -337,17 +501,18 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int ntiles = (L - i_begin + kBR - 1) / kBR;
   const uint16_t* qbase = a.q + (int64_t)start * ld + (int64_t)h * D;
   const uint16_t* gbase = a.dout + (int64_t)start * hd + (int64_t)h * D;
-  const float* lbase = a.lse + (int64_t)start * a.H + h;
+  const float* lbase = a.lse2 + (int64_t)start * a.H + h;
   const float* dbase = a.delta + (int64_t)start * a.H + h;
+  const uint32_t qs0 = lds_addr(qs), gs0 = lds_addr(gs), ls0 = lds_addr(ls), dls0 = lds_addr(dls);
 
   auto issue_tile = [&](int i0, int buf) {
     const int rows = min(kBR, L - i0);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qbase + (int64_t)i0 * ld, (uint32_t)(rows - 1) * row_bytes + D * 2);
     const __amdgpu_buffer_rsrc_t gr = make_rsrc(gbase + (int64_t)i0 * hd, (uint32_t)(rows - 1) * grow_bytes + D * 2);
 #pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) {
-      T::load(qr, qs[buf], row_bytes, u * kWaves + w, lane);
-      T::load(gr, gs[buf], grow_bytes, u * kWaves + w, lane);
+    for (int u = 0; u < T::kBlocks / kWaves; ++u) {
+      T::load(qr, qs0 + buf * T::kBytes, row_bytes, u * kWaves + w, lane);
+      T::load(gr, gs0 + buf * T::kBytes, grow_bytes, u * kWaves + w, lane);
     }
     if (w == 0) {
       const __amdgpu_buffer_rsrc_t lr = make_rsrc(lbase + (int64_t)i0 * a.H, (uint32_t)(rows - 1) * a.H * 4 + 4);
@@ -358,109 +523,82 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  f32x16 dv_acc[D / 32], dk_acc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    dv_acc[dt] = f32x16{};
-    dk_acc[dt] = f32x16{};
-  }
+  const uint32_t ob0 = T::opnd_base(lane, 0), ob1 = T::opnd_base(lane, 1);
+  const uint32_t tb0 = T::tr_base(lane, 0), tb1 = T::tr_base(lane, 1);
 
   if (ntiles > 0) issue_tile(i_begin, 0);
+  if (ntiles > 1) issue_tile(i_begin + kBR, 1);
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const int i0 = i_begin + t * kBR;
-    if (t + 1 < ntiles) issue_tile(i0 + kBR, cur ^ 1);
+  f32x16 sacc, pacc;
+  dkdv_sdp<D, BF16>(st, tile_addr(qs0, gs0, ob0, ob1), 0, sacc, pacc);
 
-    // a wave whose keys all follow every query of the tile has nothing to do
-    const bool active = !CAUSAL || i0 + kBR - 1 >= kw0;
-    if (active) {
-      const uint16_t* qt_s = qs[cur];
-      const uint16_t* gt_s = gs[cur];
-      // ---- S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        sacc[qt] = f32x16{};
-        pacc[qt] = f32x16{};
-        const int r = qt * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          sacc[qt] = mfma32<BF16>(lds_read16(qt_s + T::at(r, 16 * s + 8 * h2)), kf[s], sacc[qt]);
-          pacc[qt] = mfma32<BF16>(lds_read16(gt_s + T::at(r, 16 * s + 8 * h2)), vf[s], pacc[qt]);
-        }
-      }
-      // ---- P, Z, dS; register r of tile qt: query i0 + qt*32 + 8*(r/4) + 4*h2 + r%4
-      const bool need_mask = CAUSAL && i0 < kw0 + 31;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qrow = qt * 32 + 8 * g + 4 * h2;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&ls[cur][qrow]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dls[cur][qrow]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qt][r], a.scale_log2, -l4[e] * kLog2e));
-            if (need_mask && kj > i0 + qrow + e) p = 0.f;
-            float dp = pacc[qt][r];
-            float z = p;
-            if constexpr (DROPOUT) {
-              const float kfac = keep_factor(a, b, h, i0 + qrow + e, kj);
-              dp *= kfac;
-              z = p * kfac;
-            }
-            sacc[qt][r] = z;                 // Z (= P without dropout)
-            pacc[qt][r] = p * (dp - d4[e]);  // dS
-          }
-        }
-      // ---- dV += Z^T dO, dK += dS^T Q over four 16-query slices
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int qt = m >> 1;
-        const int sub = (m & 1) * 8;
-        const u32x4 zf = {pack2<BF16>(sacc[qt][sub + 0], sacc[qt][sub + 1]),
-                          pack2<BF16>(sacc[qt][sub + 2], sacc[qt][sub + 3]),
-                          pack2<BF16>(sacc[qt][sub + 4], sacc[qt][sub + 5]),
-                          pack2<BF16>(sacc[qt][sub + 6], sacc[qt][sub + 7])};
-        const u32x4 sf = {pack2<BF16>(pacc[qt][sub + 0], pacc[qt][sub + 1]),
-                          pack2<BF16>(pacc[qt][sub + 2], pacc[qt][sub + 3]),
-                          pack2<BF16>(pacc[qt][sub + 4], pacc[qt][sub + 5]),
-                          pack2<BF16>(pacc[qt][sub + 6], pacc[qt][sub + 7])};
-        const int row = 16 * m + 4 * h2 + (sl >> 2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int col = dt * 32 + c0 + 4 * (sl & 3);
-          const u32x2 g0 = lds_read_tr(gt_s + T::at(row, col));
-          const u32x2 g1 = lds_read_tr(gt_s + T::at(row + 8, col));
-          dv_acc[dt] = mfma32<BF16>(zf, u32x4{g0[0], g0[1], g1[0], g1[1]}, dv_acc[dt]);
-          const u32x2 x0 = lds_read_tr(qt_s + T::at(row, col));
-          const u32x2 x1 = lds_read_tr(qt_s + T::at(row + 8, col));
-          dk_acc[dt] = mfma32<BF16>(sf, u32x4{x0[0], x0[1], x1[0], x1[1]}, dk_acc[dt]);
-        }
-      }
-    }
+  auto iteration = [&](int t, auto mask) {
+    constexpr bool kMask = decltype(mask)::value;
+    const int buf = t % kNB;
+    const int nbuf = (t + 1) % kNB;
+    const int i0 = i_begin + t * kBR;
+    // tile t + 1 has landed; every wave is done with tile t - 1's buffers
     wait_vmem();
     __syncthreads();
+    if (t + 2 < ntiles) issue_tile(i0 + 2 * kBR, (t + 2) % kNB);
+
+    const uint32_t qb = qs0 + buf * T::kBytes, gb = gs0 + buf * T::kBytes;
+    const uint32_t nqb = qs0 + nbuf * T::kBytes, ngb = gs0 + nbuf * T::kBytes;
+    const TileAddr op = tile_addr(qb, gb, ob0, ob1), tr = tile_addr(qb, gb, tb0, tb1);
+    const TileAddr nop = tile_addr(nqb, ngb, ob0, ob1);
+    uint32_t lb = ls0 + buf * kBR * 4 + 16 * h2, db = dls0 + buf * kBR * 4 + 16 * h2;
+    asm volatile("" : "+v"(lb), "+v"(db));
+    // On the last tile the look-ahead products read a stale buffer and are
+    // discarded; computing them anyway keeps the tile one basic block.
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, op, 1, tr, 0, lb, db, i0, kj, h2, b, h);
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, nop, 0, tr, 1, lb, db, i0, kj, h2, b, h);
+  };
+  // Causal: only the first two tiles (queries j0 .. j0+127) hold queries
+  // before some key of the block, so only they are masked.
+  int t = 0;
+  if (CAUSAL)
+    for (; t < min(ntiles, 2); ++t) iteration(t, std::true_type{});
+  for (; t < ntiles; ++t) iteration(t, std::false_type{});
+
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    asm volatile("" : "+a"(st.dv[dt]));
+    asm volatile("" : "+a"(st.dk[dt]));
   }
 
-  // ---- epilogue: register r of tile dt holds key kw0 + 8*(r/4) + 4*h2 + r%4,
-  // head-dim element dt*32 + l32
+  // ---- epilogue: dK = scale * dK, dV, staged through LDS as [key][d] rows
+  // (register r of tile dt: key 8*(r/4) + 4*h2 + r%4 of the wave, element
+  // dt*32 + l32), then written back 16 bytes per lane.
+  __syncthreads();
+  constexpr int kRowE = D + 8;  // padded LDS row, 16-bit elements
+  uint16_t* stage_k = qs[0];    // 128 rows x kRowE elements fit in each set of tile buffers
+  uint16_t* stage_v = gs[0];
+  static_assert(kBKV * kRowE <= kNB * T::kElems, "epilogue staging does not fit");
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int j = kw0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-      if (j < L) {
-        const int64_t off = (int64_t)(start + j) * ld + (int64_t)h * D + dt * 32 + l32;
-        const uint32_t pk = pack2<BF16>(dk_acc[dt][r] * a.scale, dv_acc[dt][r]);
-        a.dk[off] = (uint16_t)(pk & 0xffff);
-        a.dv[off] = (uint16_t)(pk >> 16);
-      }
+      const int row = 32 * w + 8 * (r >> 2) + 4 * h2 + (r & 3);
+      const uint32_t pk = pack2<BF16>(st.dk[dt][r] * a.scale, st.dv[dt][r]);
+      stage_k[row * kRowE + dt * 32 + l32] = (uint16_t)(pk & 0xffff);
+      stage_v[row * kRowE + dt * 32 + l32] = (uint16_t)(pk >> 16);
     }
+  __syncthreads();
+  constexpr int kCPR = D / 8;
+#pragma unroll
+  for (int u = 0; u < kBKV * kCPR / kThreads; ++u) {
+    const int c = tid + kThreads * u;
+    const int row = c / kCPR;
+    const int col = (c % kCPR) * 8;
+    const int j = j0 + row;
+    if (j < L) {
+      const int64_t off = (int64_t)(start + j) * ld + (int64_t)h * D + col;
+      *reinterpret_cast<u32x4*>(a.dk + off) = *reinterpret_cast<const u32x4*>(&stage_k[row * kRowE + col]);
+      *reinterpret_cast<u32x4*>(a.dv + off) = *reinterpret_cast<const u32x4*>(&stage_v[row * kRowE + col]);
+    }
+  }
 }
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
@@ -493,7 +631,7 @@ hipError_t launch_bwd_d(const AttnShape& s, const BwdArgs& args, int stages, hip
 
 hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           int stages, hipStream_t stream) {
+                           float* lse2, int stages, hipStream_t stream) {
   BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -505,6 +643,7 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.delta = delta;
+  a.lse2 = lse2;
   a.cu = s.cu;
   a.ld = s.ld;
   a.B = s.B;

@@ -70,8 +70,14 @@ __device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
 // Buffer resource over `bytes` bytes from `base`: raw buffer loads at
 // offsets at or past `bytes` return zeros (the hardware range check), which is
 // how ragged tails are zero-filled without branches.
+// base and bytes must be wave-uniform; they are read from the first lane so
+// that the descriptor is known to live in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // 16-byte buffer load of every lane straight into LDS: lane l's 16 bytes land
@@ -95,6 +101,19 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, cons
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+}
+
+__device__ __forceinline__ void buffer_load_lds16_addr(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voffset) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voffset), "s"(r)
+      : "memory");
 }
 
 // 4-byte buffer load of every lane straight into LDS: lane l's 4 bytes land
@@ -136,6 +155,68 @@ struct SwzTile {
     const int c = (p % kCPR) ^ swz(r);
     buffer_load_lds16(rsrc, tile + u * 512, (uint32_t)r * row_bytes + 16 * c);
   }
+};
+
+// LDS address (bytes) of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)addr;
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A tile of ROWS rows (a multiple of 32) of D 16-bit elements in LDS, laid
+// out for the two ways the MFMA loops read it:
+//   - operand read: lane l of a wave takes the 16-byte chunk 2s + l/32 of row
+//     32g + l%32 (a 32x32x16 A or B operand with rows on lanes);
+//   - transpose read (ds_read_b64_tr_b16): 16 lanes take four consecutive
+//     elements each of 4 rows, so that every lane receives one column of a
+//     4-row slice (an operand with rows on the K dimension).
+// The tile is split into 1 KB blocks, block (g, s) holding chunks 2s, 2s + 1
+// of rows 32g .. 32g + 31; inside a block, logical slot x = row%32 + 32*(chunk
+// % 2) sits at physical 16-byte slot x ^ 4*(x/32) ^ 8*(s%2).  An operand read
+// is then 64 consecutive slots (permuted inside each 16-slot group), and a
+// transpose read hits 32 different 8-byte bank pairs per half-wave, so
+// neither conflicts with 64 four-byte banks; and every read of a loop is one
+// per-lane base register plus an immediate offset.  Blocks are filled whole
+// by 1 KB direct-to-LDS loads (lane l writes physical slot l).
+template <int D, int ROWS>
+struct MTile {
+  static constexpr int kSPR = D / 16;                  // blocks per 32-row group
+  static constexpr int kBlocks = ROWS / 32 * kSPR;     // = number of 1 KB loads
+  static constexpr int kElems = kBlocks * 512;         // 16-bit elements
+  static constexpr int kBytes = kBlocks * 1024;
+
+  // Load block u: lane l fetches the chunk that belongs at physical slot l.
+  // row_bytes apart rows; rows the buffer range does not cover read as 0.
+  __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t tile_addr, uint32_t row_bytes,
+                                              int u, int lane) {
+    const int s = u % kSPR;
+    const int g = u / kSPR;
+    const int x = lane ^ ((lane >> 5) << 2) ^ ((s & 1) << 3);
+    const uint32_t off = (uint32_t)(32 * g + (x & 31)) * row_bytes + 16 * (2 * s + (x >> 5));
+    buffer_load_lds16_addr(rsrc, tile_addr + 1024 * u, off);
+  }
+  // Operand read of block (g, s) = tile + opnd_off(g, s) + opnd_base(lane, s % 2).
+  __device__ static __forceinline__ uint32_t opnd_base(int lane, int sodd) {
+    return 16 * (lane ^ ((lane >> 5) << 2) ^ (sodd << 3));
+  }
+  static constexpr uint32_t opnd_off(int g, int s) { return 1024 * (g * kSPR + s); }
+  // Transpose read of rows 16m + 8hi + 4*(lane/32) + 0..3, columns 32dt + lane%32:
+  // tile + tr_off(m, dt) + tr_base(lane, hi).
+  __device__ static __forceinline__ uint32_t tr_base(int lane, int hi) {
+    const int g = (lane >> 4) & 1, h2 = lane >> 5, sl = lane & 15;
+    const int e = sl >> 2, f = (sl >> 1) & 1, half = sl & 1;
+    const int x = (8 * hi + 4 * h2 + e + 32 * f) ^ (4 * f) ^ (8 * g);
+    return 1024 * g + 16 * x + 8 * half;
+  }
+  static constexpr uint32_t tr_off(int m, int dt) { return 1024 * ((m >> 1) * kSPR + 2 * dt) + 256 * (m & 1); }
 };
 
 // Wait until this wave's outstanding vector-memory operations (including

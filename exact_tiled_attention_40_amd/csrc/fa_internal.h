@@ -25,7 +25,8 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
 
 hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, float* delta, int stages, hipStream_t stream);
+                           void* dv, float* delta, float* lse2, int stages,
+                           hipStream_t stream);
 
 // Stage bits of launch_backward: the dQ kernel (which also writes D) and the
 // dK/dV kernel (which reads D).
