@@ -41,9 +41,11 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;          // dK/dV kernel: one wave per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 32 * kWaves;   // queries per dQ workgroup
+constexpr int kWavesQ = 4;         // dQ kernel: two workgroups (waves) per SIMD
+constexpr int kThreadsQ = 64 * kWavesQ;
+constexpr int kBQ = 32 * kWavesQ;  // queries per dQ workgroup
 constexpr int kBC = 64;            // keys per tile of the dQ kernel
 constexpr int kBKV = 32 * kWaves;  // keys per dK/dV workgroup
 constexpr int kBR = 64;            // queries per tile of the dK/dV kernel
@@ -93,9 +95,11 @@ __device__ __forceinline__ float keep_factor(const BwdArgs& a, int b, int h, int
 
 // ---------------------------------------------------------------- dQ (+ D)
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
-  using T = SwzTile<D, kBC>;
-  constexpr int kLoadsPerWave = T::kLoads / kWaves;
+__global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+  using T = MTile<D, kBC>;
+  constexpr int kNS = 2 * (D / 16);  // S^T and dP^T products per 32-key half (D/16 k-steps each)
+  constexpr int kNQ = 2 * (D / 32);  // dQ^T products per 32-key half (two 16-key slices x D/32 tiles)
+  constexpr int kPF = 2;             // LDS operand reads in flight (products ahead)
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
 
@@ -104,9 +108,6 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
-  const int grp = lane >> 4;
-  const int sl = lane & 15;
-  const int c0 = 16 * (grp & 1);
 
   // Workgroup -> (b, h, query block): heads fastest (one head's blocks share
   // an XCD when B*H is a multiple of 8); causal: longest blocks first.
@@ -175,15 +176,16 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     a.lse2[(int64_t)(start + qi) * a.H + h] = lse2;
   }
 
+  const uint32_t ks0 = lds_addr(ks), vs0 = lds_addr(vs);
   auto issue_tile = [&](int j0, int buf) {
     const int rows = min(kBC, L - j0);
     const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
 #pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) {
-      T::load(kr, ks[buf], row_bytes, u * kWaves + w, lane);
-      T::load(vr, vs[buf], row_bytes, u * kWaves + w, lane);
+    for (int u = 0; u < T::kBlocks / kWavesQ; ++u) {
+      T::load(kr, ks0 + buf * T::kBytes, row_bytes, u * kWavesQ + w, lane);
+      T::load(vr, vs0 + buf * T::kBytes, row_bytes, u * kWavesQ + w, lane);
     }
   };
 
@@ -191,73 +193,104 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) qacc[dt] = f32x16{};
 
+  const uint32_t ob0 = T::opnd_base(lane, 0), ob1 = T::opnd_base(lane, 1);
+  const uint32_t tb0 = T::tr_base(lane, 0), tb1 = T::tr_base(lane, 1);
+
   issue_tile(0, 0);
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile of 64 keys, as two 32-key halves kt.  Per half, in a fixed
+  // order (sched_barrier fences keep it): S^T = K Q^T and dP^T = V dO^T
+  // interleaved, their K/V operands read kPF products ahead; the first K^T
+  // transpose reads; P and dS; dQ^T += K^T dS^T with its K^T operands read
+  // kPF products ahead.
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
     const int cur = t & 1;
     const int j0 = t * kBC;
-    if (t + 1 < ntiles) issue_tile(j0 + kBC, cur ^ 1);
+    uint32_t k0 = ks0 + cur * T::kBytes + ob0, k1 = ks0 + cur * T::kBytes + ob1;
+    uint32_t v0 = vs0 + cur * T::kBytes + ob0, v1 = vs0 + cur * T::kBytes + ob1;
+    uint32_t kt0 = ks0 + cur * T::kBytes + tb0, kt1 = ks0 + cur * T::kBytes + tb1;
+    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1), "+v"(kt0), "+v"(kt1));
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // product i: tensor i & 1 (K for S, V for dP), k-step i >> 1
+      auto sread = [&](int i) {
+        const int s = i >> 1;
+        const uint32_t base = (i & 1) ? ((s & 1) ? v1 : v0) : ((s & 1) ? k1 : k0);
+        return lds_read16_at(base + T::opnd_off(kt, s));
+      };
+      // product j: key slice 2kt + j / (D/32), head-dim tile j % (D/32)
+      auto qread = [&](int j) {
+        const uint32_t o = T::tr_off(2 * kt + j / (D / 32), j % (D / 32));
+        const u32x2 lo = lds_read_tr_at(kt0 + o), hi = lds_read_tr_at(kt1 + o);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      u32x4 sb[kNS];
+#pragma unroll
+      for (int i = 0; i < kPF; ++i) sb[i] = sread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kNS; ++i) {
+        if (i & 1)
+          pacc = mfma32<BF16>(sb[i], gf[i >> 1], pacc);
+        else
+          sacc = mfma32<BF16>(sb[i], qf[i >> 1], sacc);
+        if (i + kPF < kNS) sb[i + kPF] = sread(i + kPF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      u32x4 qb_[kNQ];
+#pragma unroll
+      for (int j = 0; j < kPF; ++j) qb_[j] = qread(j);
 
-    const bool active = !CAUSAL || j0 <= qw + 31;
-    if (active) {
-      const uint16_t* kt_s = ks[cur];
-      const uint16_t* vt_s = vs[cur];
-      // ---- S^T = K Q^T and dP^T = V dO^T for keys j0 .. j0+63
-      f32x16 sacc[2], pacc[2];
+      // ---- P and dS; register r: key j0 + kt*32 + 8*(r/4) + 4*h2 + r%4
+      uint32_t spk[8];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x16{};
-        pacc[kt] = f32x16{};
-        const int r = kt * 32 + l32;
+      for (int g = 0; g < 4; ++g) {
+        const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
+        Philox4 rnd;
+        if constexpr (DROPOUT)
+          rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
+        float ds[4];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          sacc[kt] = mfma32<BF16>(lds_read16(kt_s + T::at(r, 16 * s + 8 * h2)), qf[s], sacc[kt]);
-          pacc[kt] = mfma32<BF16>(lds_read16(vt_s + T::at(r, 16 * s + 8 * h2)), gf[s], pacc[kt]);
-        }
-      }
-      // ---- P and dS; register r of tile kt: key j0 + kt*32 + 8*(r/4) + 4*h2 + r%4
-      const bool need_mask = (CAUSAL && j0 + kBC - 1 > qw) || (j0 + kBC > L);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
-          Philox4 rnd;
-          if constexpr (DROPOUT)
-            rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], a.scale_log2, -lse2));
-            if (need_mask && ((CAUSAL && kj4 + e > qi) || kj4 + e >= L)) p = 0.f;
-            float dp = pacc[kt][r];
-            if constexpr (DROPOUT) {
-              const uint32_t word = e == 0 ? rnd.x : e == 1 ? rnd.y : e == 2 ? rnd.z : rnd.w;
-              dp *= word >= a.drop_thresh ? a.drop_rescale : 0.f;
-            }
-            sacc[kt][r] = p * (dp - delta);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, -lse2));
+          if (kMask && ((CAUSAL && kj4 + e > qi) || kj4 + e >= L)) p = 0.f;
+          float dp = pacc[r];
+          if constexpr (DROPOUT) {
+            const uint32_t word = e == 0 ? rnd.x : e == 1 ? rnd.y : e == 2 ? rnd.z : rnd.w;
+            dp *= word >= a.drop_thresh ? a.drop_rescale : 0.f;
           }
+          ds[e] = p * (dp - delta);
         }
-      // ---- dQ^T += K^T dS^T, four 16-key slices
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int kt = m >> 1;
-        const int sub = (m & 1) * 8;
-        const u32x4 sf = {pack2<BF16>(sacc[kt][sub + 0], sacc[kt][sub + 1]),
-                          pack2<BF16>(sacc[kt][sub + 2], sacc[kt][sub + 3]),
-                          pack2<BF16>(sacc[kt][sub + 4], sacc[kt][sub + 5]),
-                          pack2<BF16>(sacc[kt][sub + 6], sacc[kt][sub + 7])};
-        const int row = 16 * m + 4 * h2 + (sl >> 2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int col = dt * 32 + c0 + 4 * (sl & 3);
-          const u32x2 lo = lds_read_tr(kt_s + T::at(row, col));
-          const u32x2 hi = lds_read_tr(kt_s + T::at(row + 8, col));
-          qacc[dt] = mfma32<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf, qacc[dt]);
-        }
+        spk[2 * g] = pack2<BF16>(ds[0], ds[1]);
+        spk[2 * g + 1] = pack2<BF16>(ds[2], ds[3]);
       }
+      const u32x4 sf[2] = {u32x4{spk[0], spk[1], spk[2], spk[3]}, u32x4{spk[4], spk[5], spk[6], spk[7]}};
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- dQ^T += K^T dS^T over the two 16-key slices of this half
+#pragma unroll
+      for (int j = 0; j < kNQ; ++j) {
+        qacc[j % (D / 32)] = mfma32<BF16>(qb_[j], sf[j / (D / 32)], qacc[j % (D / 32)]);
+        if (j + kPF < kNQ) qb_[j + kPF] = qread(j + kPF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kBC;
+    if (t + 1 < ntiles) issue_tile(j0 + kBC, (t & 1) ^ 1);
+    // a wave whose queries all precede the tile has nothing to do in it
+    if (!CAUSAL || j0 <= qw + 31) {
+      if ((CAUSAL && j0 + kBC - 1 > qw) || j0 + kBC > L)
+        tile(t, std::true_type{});
+      else
+        tile(t, std::false_type{});
     }
     wait_vmem();
     __syncthreads();
@@ -321,45 +354,82 @@ __device__ __forceinline__ void dkdv_sdp(const KVState<D, BF16>& st, const TileA
   }
 }
 
-// One 32-query half (queries 32qt .. 32qt+31 of the tile at tr) of the
-// pipeline, in a fixed instruction order (sched_barrier fences keep the
-// compiler from regrouping it):
-//   phase 1: the look-ahead products S, dP of half nqt of the tile at nop,
-//            their LDS operands read kPF products ahead, with this half's
-//            P, Z, dS (from sacc, pacc) computed element by element between
-//            them;
-//   phase 2: dV += Z^T dO and dK += dS^T Q for this half, the transpose reads
-//            of each product issued kPF2 products ahead.
-// On return sacc, pacc hold the look-ahead S, dP.  Register r of sacc holds
-// query 32qt + 8*(r/4) + 4*(lane/32) + r%4 of this lane's key; lb, db point at
-// LSE*log2(e) and D of the tile, offset by this lane half's first query.
+// Where a 32-query half lives: its tile's LSE*log2(e) and D in LDS (offset
+// by this lane half's first query), the tile's first query, and which half.
+struct HalfCtx {
+  uint32_t lb, db;
+  int i0, qt;
+};
+
+// P, Z and dS of element r of a half (register r of S, dP: query
+// 32qt + 8*(r/4) + 4*(lane/32) + r%4 of this lane's key kj).
+template <bool MASK, bool DROPOUT>
+__device__ __forceinline__ void dkdv_elem(const BwdArgs& a, float s, float dp, float lse2, float dd, const HalfCtx& c,
+                                          int r, int kj, int h2, int b, int h, float& z, float& ds) {
+  const int qi = c.i0 + c.qt * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+  float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, a.scale_log2, -lse2));
+  if (MASK && kj > qi) p = 0.f;
+  z = p;
+  if constexpr (DROPOUT) {
+    const float kfac = keep_factor(a, b, h, qi, kj);
+    dp *= kfac;
+    z = p * kfac;
+  }
+  ds = p * (dp - dd);
+}
+
+__device__ __forceinline__ f32x4 lds_f32x4(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)addr;
+}
+
+// One 32-query half h of the pipeline, in a fixed instruction order
+// (sched_barrier fences keep the compiler from regrouping it).  On entry
+// sacc, pacc hold S, dP of h and zpk/spk its packed Z, dS pairs 0..3
+// (elements 0..7).
+//   phase 1: the look-ahead products S, dP of the next half (operands of half
+//            nqt of the tile at nop, read kPF products ahead), with elements
+//            8..15 of h computed between them;
+//   phase 2: dV += Z^T dO and dK += dS^T Q for h (transpose reads kPF2
+//            products ahead), with elements 0..7 of the next half computed
+//            between them once its S, dP are complete.
+// Either phase then carries about three VALU instructions per product, few
+// enough for the wave to issue them while its products run.  On return
+// sacc, pacc, zpk[0..3], spk[0..3] describe the next half.
 template <int D, bool BF16, bool MASK, bool DROPOUT>
 __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st, f32x16& sacc, f32x16& pacc,
-                                          const TileAddr& nop, int nqt, const TileAddr& tr, int qt, uint32_t lb,
-                                          uint32_t db, int i0, int kj, int h2, int b, int h) {
+                                          uint32_t (&zpk)[8], uint32_t (&spk)[8], u32x4 (&pf)[4],
+                                          const TileAddr& nop, const TileAddr& nnop, int nnqt, const TileAddr& tr,
+                                          const HalfCtx& cur, const HalfCtx& nxt, int kj, int h2, int b, int h) {
   using T = MTile<D, kBR>;
-  constexpr int kNP = D / 8;   // look-ahead products (S and dP, D/16 k-steps each)
-  constexpr int kPF = 4;       // operand reads in flight
-  constexpr int kEPP = 16 / kNP;  // softmax elements per product
-  auto opnd = [&](int i) {
+  constexpr int kNP = D / 8;  // look-ahead products (S and dP, D/16 k-steps each)
+  constexpr int kPF = 4;      // LDS operand reads in flight (products ahead)
+  static_assert(kNP >= 2 * kPF, "prefetch window exceeds a phase");
+  auto opnd = [&](const TileAddr& t, int qt, int i) {
     const int s = i >> 1;
-    const uint32_t base = (i & 1) ? ((s & 1) ? nop.g1 : nop.g0) : ((s & 1) ? nop.q1 : nop.q0);
-    return lds_read16_at(base + T::opnd_off(nqt, s));
+    const uint32_t base = (i & 1) ? ((s & 1) ? t.g1 : t.g0) : ((s & 1) ? t.q1 : t.q0);
+    return lds_read16_at(base + T::opnd_off(qt, s));
+  };
+  constexpr int kNA = 2 * 2 * (D / 32);  // dV, dK products
+  auto tr_pair = [&](int j) {
+    const int mm = j / (2 * (D / 32)), dt = (j >> 1) % (D / 32);
+    const uint32_t o = T::tr_off(2 * cur.qt + mm, dt);
+    const uint32_t b0 = (j & 1) ? tr.q0 : tr.g0, b1 = (j & 1) ? tr.q1 : tr.g1;
+    const u32x2 x0 = lds_read_tr_at(b0 + o), x1 = lds_read_tr_at(b1 + o);
+    return u32x4{x0[0], x0[1], x1[0], x1[1]};
   };
 
-  // ---- phase 1
-  auto lse_d = [&](int g, f32x4& l, f32x4& d) {
-    l = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(lb + 4 * (qt * 32 + 8 * g));
-    d = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(db + 4 * (qt * 32 + 8 * g));
-  };
+  // ---- phase 1: look-ahead S, dP; elements 8..15 of h.  Operands 0..3
+  // arrive in pf (read during the previous half); the last steps start the
+  // transpose reads of phase 2.
   u32x4 ob[kNP];
-  f32x4 l4, d4, l4n, d4n;
+  u32x4 tb[kNA];
 #pragma unroll
-  for (int i = 0; i < kPF; ++i) ob[i] = opnd(i);
-  lse_d(0, l4, d4);
+  for (int i = 0; i < kPF; ++i) ob[i] = pf[i];
+  const int qoff = cur.qt * 32;
+  f32x4 l4a = lds_f32x4(cur.lb + 4 * (qoff + 16)), d4a = lds_f32x4(cur.db + 4 * (qoff + 16));
+  f32x4 l4b = lds_f32x4(cur.lb + 4 * (qoff + 24)), d4b = lds_f32x4(cur.db + 4 * (qoff + 24));
   __builtin_amdgcn_sched_barrier(0);
   f32x16 ns = f32x16{}, np = f32x16{};
-  uint32_t zpk[8], spk[8];  // packed Z, dS pairs (elements 2k, 2k + 1)
   float zprev = 0.f, dsprev = 0.f;
 #pragma unroll
   for (int i = 0; i < kNP; ++i) {
@@ -368,55 +438,38 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
       np = mfma32<BF16>(ob[i], st.vf[s], np);
     else
       ns = mfma32<BF16>(ob[i], st.kf[s], ns);
-    if (i + kPF < kNP) ob[i + kPF] = opnd(i + kPF);
+    if (i + kPF < kNP)
+      ob[i + kPF] = opnd(nop, nxt.qt, i + kPF);
+    else
+      tb[i + kPF - kNP] = tr_pair(i + kPF - kNP);
 #pragma unroll
-    for (int u = 0; u < kEPP; ++u) {
-      const int r = i * kEPP + u;
-      const int g = r >> 2, e = r & 3;
-      if (e == 0 && g < 3) lse_d(g + 1, l4n, d4n);  // next group's LSE, D, four elements ahead
-      const int qrow = qt * 32 + 8 * g + 4 * h2 + e;
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, -l4[e]));
-      if (MASK && kj > i0 + qrow) p = 0.f;
-      float dp = pacc[r];
-      float zz = p;
-      if constexpr (DROPOUT) {
-        const float kfac = keep_factor(a, b, h, i0 + qrow, kj);
-        dp *= kfac;
-        zz = p * kfac;
-      }
-      const float dsv = p * (dp - d4[e]);
+    for (int r = 8 + (i * 8) / kNP; r < 8 + ((i + 1) * 8) / kNP; ++r) {
+      const f32x4& l4 = r < 12 ? l4a : l4b;
+      const f32x4& d4 = r < 12 ? d4a : d4b;
+      float z, ds;
+      dkdv_elem<MASK, DROPOUT>(a, sacc[r], pacc[r], l4[r & 3], d4[r & 3], cur, r, kj, h2, b, h, z, ds);
       if (r & 1) {
-        zpk[r >> 1] = pack2<BF16>(zprev, zz);
-        spk[r >> 1] = pack2<BF16>(dsprev, dsv);
+        zpk[r >> 1] = pack2<BF16>(zprev, z);
+        spk[r >> 1] = pack2<BF16>(dsprev, ds);
       } else {
-        zprev = zz;
-        dsprev = dsv;
-      }
-      if (e == 3) {
-        l4 = l4n;
-        d4 = d4n;
+        zprev = z;
+        dsprev = ds;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  sacc = ns;
-  pacc = np;
   const u32x4 zf[2] = {u32x4{zpk[0], zpk[1], zpk[2], zpk[3]}, u32x4{zpk[4], zpk[5], zpk[6], zpk[7]}};
   const u32x4 sf[2] = {u32x4{spk[0], spk[1], spk[2], spk[3]}, u32x4{spk[4], spk[5], spk[6], spk[7]}};
 
-  // ---- phase 2: product j = (slice mm, head-dim tile dt, dV or dK)
-  constexpr int kNA = 2 * 2 * (D / 32);
-  constexpr int kPF2 = 4;
-  auto tr_pair = [&](int j) {
-    const int mm = j / (2 * (D / 32)), dt = (j >> 1) % (D / 32);
-    const uint32_t o = T::tr_off(2 * qt + mm, dt);
-    const uint32_t b0 = (j & 1) ? tr.q0 : tr.g0, b1 = (j & 1) ? tr.q1 : tr.g1;
-    const u32x2 x0 = lds_read_tr_at(b0 + o), x1 = lds_read_tr_at(b1 + o);
-    return u32x4{x0[0], x0[1], x1[0], x1[1]};
-  };
-  u32x4 tb[kNA];
-#pragma unroll
-  for (int j = 0; j < kPF2; ++j) tb[j] = tr_pair(j);
+  // ---- phase 2: product j = (slice mm, head-dim tile dt, dV or dK) of h;
+  // elements 0..7 of the next half, starting once ns, np are complete; the
+  // last steps read the first operands of the next half's look-ahead
+  // products (half nnqt of the tile at nnop) into pf.
+  constexpr int kLag = 2;  // products to wait before reading ns, np
+  static_assert(kNA >= 2 * kPF, "prefetch window exceeds a phase");
+  const int noff = nxt.qt * 32;
+  f32x4 l4c = lds_f32x4(nxt.lb + 4 * noff), d4c = lds_f32x4(nxt.db + 4 * noff);
+  f32x4 l4d = lds_f32x4(nxt.lb + 4 * (noff + 8)), d4d = lds_f32x4(nxt.db + 4 * (noff + 8));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kNA; ++j) {
@@ -425,9 +478,31 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
       st.dk[dt] = mfma32<BF16>(sf[mm], tb[j], st.dk[dt]);
     else
       st.dv[dt] = mfma32<BF16>(zf[mm], tb[j], st.dv[dt]);
-    if (j + kPF2 < kNA) tb[j + kPF2] = tr_pair(j + kPF2);
+    if (j + kPF < kNA)
+      tb[j + kPF] = tr_pair(j + kPF);
+    else
+      pf[j + kPF - kNA] = opnd(nnop, nnqt, j + kPF - kNA);
+    if (j >= kLag) {
+      constexpr int kSpan = kNA - kLag;
+#pragma unroll
+      for (int r = ((j - kLag) * 8) / kSpan; r < ((j - kLag + 1) * 8) / kSpan; ++r) {
+        const f32x4& l4 = r < 4 ? l4c : l4d;
+        const f32x4& d4 = r < 4 ? d4c : d4d;
+        float z, ds;
+        dkdv_elem<MASK, DROPOUT>(a, ns[r], np[r], l4[r & 3], d4[r & 3], nxt, r, kj, h2, b, h, z, ds);
+        if (r & 1) {
+          zpk[r >> 1] = pack2<BF16>(zprev, z);
+          spk[r >> 1] = pack2<BF16>(dsprev, ds);
+        } else {
+          zprev = z;
+          dsprev = ds;
+        }
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
+  sacc = ns;
+  pacc = np;
 }
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
@@ -531,8 +606,36 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   wait_vmem();
   __syncthreads();
 
+  // pipeline prologue: S, dP and elements 0..7 of the first half, and the
+  // first operands of its look-ahead products (half 1 of tile 0)
   f32x16 sacc, pacc;
-  dkdv_sdp<D, BF16>(st, tile_addr(qs0, gs0, ob0, ob1), 0, sacc, pacc);
+  uint32_t zpk[8], spk[8];
+  u32x4 pf[4];
+  const TileAddr op0 = tile_addr(qs0, gs0, ob0, ob1);
+  dkdv_sdp<D, BF16>(st, op0, 0, sacc, pacc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = i >> 1;
+    const uint32_t base = (i & 1) ? ((s & 1) ? op0.g1 : op0.g0) : ((s & 1) ? op0.q1 : op0.q0);
+    pf[i] = lds_read16_at(base + T::opnd_off(1, s));
+  }
+  {
+    const HalfCtx c0{ls0 + 16 * h2, dls0 + 16 * h2, i_begin, 0};
+    float zprev = 0.f, dsprev = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const f32x4 l4 = lds_f32x4(c0.lb + 4 * 8 * (r >> 2)), d4 = lds_f32x4(c0.db + 4 * 8 * (r >> 2));
+      float z, ds;
+      dkdv_elem<CAUSAL, DROPOUT>(a, sacc[r], pacc[r], l4[r & 3], d4[r & 3], c0, r, kj, h2, b, h, z, ds);
+      if (r & 1) {
+        zpk[r >> 1] = pack2<BF16>(zprev, z);
+        spk[r >> 1] = pack2<BF16>(dsprev, ds);
+      } else {
+        zprev = z;
+        dsprev = ds;
+      }
+    }
+  }
 
   auto iteration = [&](int t, auto mask) {
     constexpr bool kMask = decltype(mask)::value;
@@ -540,8 +643,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const int nbuf = (t + 1) % kNB;
     const int i0 = i_begin + t * kBR;
     // tile t + 1 has landed; every wave is done with tile t - 1's buffers
+    // (the reads still in flight here touch tiles t and t + 1 only)
     wait_vmem();
-    __syncthreads();
+    barrier_keep_lds_reads();
     if (t + 2 < ntiles) issue_tile(i0 + 2 * kBR, (t + 2) % kNB);
 
     const uint32_t qb = qs0 + buf * T::kBytes, gb = gs0 + buf * T::kBytes;
@@ -549,11 +653,15 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const TileAddr op = tile_addr(qb, gb, ob0, ob1), tr = tile_addr(qb, gb, tb0, tb1);
     const TileAddr nop = tile_addr(nqb, ngb, ob0, ob1);
     uint32_t lb = ls0 + buf * kBR * 4 + 16 * h2, db = dls0 + buf * kBR * 4 + 16 * h2;
-    asm volatile("" : "+v"(lb), "+v"(db));
-    // On the last tile the look-ahead products read a stale buffer and are
-    // discarded; computing them anyway keeps the tile one basic block.
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, op, 1, tr, 0, lb, db, i0, kj, h2, b, h);
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, nop, 0, tr, 1, lb, db, i0, kj, h2, b, h);
+    uint32_t nlb = ls0 + nbuf * kBR * 4 + 16 * h2, ndb = dls0 + nbuf * kBR * 4 + 16 * h2;
+    asm volatile("" : "+v"(lb), "+v"(db), "+v"(nlb), "+v"(ndb));
+    const HalfCtx h0{lb, db, i0, 0}, h1{lb, db, i0, 1}, n0{nlb, ndb, i0 + kBR, 0};
+    // On the last tile the look-ahead work reads a stale buffer and is
+    // discarded; doing it anyway keeps the tile one basic block.  Masked
+    // tiles come first, so the look-ahead into the next tile may use this
+    // tile's masking.
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj, h2, b, h);
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2, b, h);
   };
   // Causal: only the first two tiles (queries j0 .. j0+127) hold queries
   // before some key of the block, so only they are masked.
@@ -606,7 +714,7 @@ hipError_t launch_bwd_t(const AttnShape& s, const BwdArgs& args, int stages, hip
   if (stages & kBwdDq) {
     const int64_t nb = (int64_t)args.nqb * s.B * s.H;
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT>), dim3((unsigned)nb), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT>), dim3((unsigned)nb), dim3(kThreadsQ), 0, stream,
                        args);
   }
   if (stages & kBwdKV) {

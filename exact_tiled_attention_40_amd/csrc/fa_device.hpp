@@ -223,6 +223,12 @@ struct MTile {
 // direct-to-LDS loads) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier without the LDS fence of __syncthreads(), for loops whose
+// only LDS writes are direct-to-LDS loads (completed by wait_vmem() before
+// the barrier): LDS reads issued before it may stay in flight.  The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_lds_reads() { asm volatile("s_barrier" ::: "memory"); }
+
 // v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b.
 // Written as inline assembly because the compiler's builtin for it returns
 // the first operand for both results.  The s_nop covers the VALU-write ->

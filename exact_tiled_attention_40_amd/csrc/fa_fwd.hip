@@ -1,14 +1,18 @@
 // Fused exact attention forward for gfx950 (MI355X).
 //
 // One workgroup = one (batch-or-sequence b, head h, block of kBR queries);
-// four waves, each owning 32 consecutive queries.  The kernel walks the key
-// blocks the block needs (all of them, or only those left of the diagonal
-// when causal), which is the tiling of the lab write-up "FlashAttention"
-// (dpshk.com), section 3.1, with QK^T, softmax and PV fused as in the
-// tiemojia.cn article's "kernel fusion" paragraph:
-//   - K and V tiles (kBC keys) are staged HBM -> registers -> LDS, double
-//     buffered: the next tile's global loads are in flight while the current
-//     tile is consumed.
+// eight waves (two per SIMD, so one wave's softmax overlaps the other's
+// matrix products), each owning 32 consecutive queries.  The kernel walks the
+// key blocks the block needs (all of them, or only those left of the
+// diagonal when causal), which is the tiling of the lab write-up
+// "FlashAttention" (dpshk.com), section 3.1, with QK^T, softmax and PV fused
+// as in the tiemojia.cn article's "kernel fusion" paragraph:
+//   - K and V tiles (kBC keys) go straight from HBM to LDS (direct buffer
+//     loads), double buffered: the next tile's loads are in flight while the
+//     current tile is consumed.  The tiles use the MFMA-native LDS layout of
+//     MTile, so operand and transpose reads are conflict-free and each is a
+//     base register plus an immediate offset; LDS operands are read a few
+//     products ahead of the product that consumes them.
 //   - The wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (Q stays in
 //     registers as the B operand).  In that orientation each lane owns one
 //     query and 16 keys per 32x32 tile, so the row max and row sum are
@@ -21,13 +25,15 @@
 //     permuted, and V is read with the same permutation), V^T comes from the
 //     LDS transpose read ds_read_b64_tr_b16.
 //   - Epilogue: O = O / l in fp32, rounded once to bf16/fp16; LSE = m + ln l.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;  // two per SIMD; 256 queries share each K/V tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;  // queries per workgroup
 constexpr int kBC = 64;           // keys per tile
@@ -53,9 +59,11 @@ struct FwdArgs {
 };
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdArgs a) {
-  using T = SwzTile<D, kBC>;
-  constexpr int kLoadsPerWave = T::kLoads / kWaves;  // 1 KB direct-to-LDS loads per wave per tensor
+__global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
+  using T = MTile<D, kBC>;
+  constexpr int kNS = 2 * (D / 16);  // S^T products per tile (two 32-key tiles x D/16 k-steps)
+  constexpr int kNO = 4 * (D / 32);  // O^T products per tile (four 16-key slices x D/32 tiles)
+  constexpr int kPF = 4;             // LDS operand reads in flight (products ahead)
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
 
@@ -115,7 +123,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdArgs a) {
     for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(qf[s]));
   }
 
-  // Direct HBM -> LDS tile load: wave w issues loads w, w + kWaves, ... of
+  const uint32_t ks0 = lds_addr(ks), vs0 = lds_addr(vs);
+  // Direct HBM -> LDS tile load: wave w issues blocks w, w + kWaves, ... of
   // each tensor's tile.
   auto issue_tile = [&](int j0, int buf) {
     const int rows = min(kBC, L - j0);
@@ -123,9 +132,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
 #pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) {
-      T::load(kr, ks[buf], row_bytes, u * kWaves + w, lane);
-      T::load(vr, vs[buf], row_bytes, u * kWaves + w, lane);
+    for (int u = 0; u < T::kBlocks / kWaves; ++u) {
+      T::load(kr, ks0 + buf * T::kBytes, row_bytes, u * kWaves + w, lane);
+      T::load(vr, vs0 + buf * T::kBytes, row_bytes, u * kWaves + w, lane);
     }
   };
 
@@ -135,103 +144,133 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // reference max, in units of log2 (scores * scale * log2 e)
   float l_run = 0.f;        // this lane's share of the row sum
 
+  const uint32_t ob0 = T::opnd_base(lane, 0), ob1 = T::opnd_base(lane, 1);
+  const uint32_t tb0 = T::tr_base(lane, 0), tb1 = T::tr_base(lane, 1);
+
   issue_tile(0, 0);
   wait_vmem();
   __syncthreads();
 
-  const int grp = lane >> 4;
-  const int sl = lane & 15;
-  const int c0 = 16 * (grp & 1);
-
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile of 64 keys.  Instruction order (sched_barrier fences keep it):
+  // the S^T products with their K operands read kPF products ahead; the first
+  // V^T transpose reads; the softmax; the O^T products with their V^T
+  // operands read kPF products ahead.
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
     const int cur = t & 1;
     const int j0 = t * kBC;
-    if (t + 1 < ntiles) issue_tile(j0 + kBC, cur ^ 1);
+    uint32_t k0 = ks0 + cur * T::kBytes + ob0, k1 = ks0 + cur * T::kBytes + ob1;
+    uint32_t v0 = vs0 + cur * T::kBytes + tb0, v1 = vs0 + cur * T::kBytes + tb1;
+    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
+    auto kread = [&](int i) {  // product i: key tile i & 1, k-step i >> 1
+      const int s = i >> 1;
+      return lds_read16_at(((s & 1) ? k1 : k0) + T::opnd_off(i & 1, s));
+    };
+    auto vread = [&](int j) {  // product j: key slice j / (D/32), head-dim tile j % (D/32)
+      const uint32_t o = T::tr_off(j / (D / 32), j % (D / 32));
+      const u32x2 lo = lds_read_tr_at(v0 + o), hi = lds_read_tr_at(v1 + o);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
 
-    // A wave whose queries all precede the tile has nothing to do in it.
-    const bool active = !CAUSAL || j0 <= qw + 31;
-    if (active) {
-      const uint16_t* kt_s = ks[cur];
-      const uint16_t* vt_s = vs[cur];
-      // ---- S^T = K Q^T for keys j0 .. j0+63 (two 32-key tiles)
-      f32x16 sacc[2];
+    // ---- S^T = K Q^T for keys j0 .. j0+63
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    u32x4 kb[kNS];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x16{};
-        const int r = kt * 32 + l32;
+    for (int i = 0; i < kPF; ++i) kb[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) sacc[kt] = mfma32<BF16>(lds_read16(kt_s + T::at(r, 16 * s + 8 * h2)), qf[s], sacc[kt]);
-      }
-      // ---- mask keys after the query (causal) and beyond the sequence end
-      const bool need_mask = (CAUSAL && j0 + kBC - 1 > qw) || (j0 + kBC > L);
-      if (need_mask) {
+    for (int i = 0; i < kNS; ++i) {
+      sacc[i & 1] = mfma32<BF16>(kb[i], qf[i >> 1], sacc[i & 1]);
+      if (i + kPF < kNS) kb[i + kPF] = kread(i + kPF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 vb[kNO];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kj = j0 + kt * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if ((CAUSAL && kj > qi) || kj >= L) sacc[kt][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax with a lazily rescaled reference max
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-      mx = halves_max(mx) * a.scale_log2;
-      const bool grow = mx > m_run + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-        m_run = grow ? mx : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float rs = 0.f;
+    for (int j = 0; j < kPF; ++j) vb[j] = vread(j);
+
+    // ---- mask keys after the query (causal) and beyond the sequence end;
+    // register r of key tile kt holds key j0 + kt*32 + 8*(r/4) + 4*h2 + r%4
+    if constexpr (kMask) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], a.scale_log2, -m_use));
-          rs += p;
-          sacc[kt][r] = p;
+          const int kj = j0 + kt * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if ((CAUSAL && kj > qi) || kj >= L) sacc[kt][r] = -INFINITY;
         }
-      l_run += rs;
-      if constexpr (DROPOUT) {
+    }
+    // ---- online softmax with a lazily rescaled reference max
+    float mx = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
-            const Philox4 rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b,
-                                              a.seed_lo, a.seed_hi);
-            if (rnd.x < a.drop_thresh) sacc[kt][4 * g + 0] = 0.f;
-            if (rnd.y < a.drop_thresh) sacc[kt][4 * g + 1] = 0.f;
-            if (rnd.z < a.drop_thresh) sacc[kt][4 * g + 2] = 0.f;
-            if (rnd.w < a.drop_thresh) sacc[kt][4 * g + 3] = 0.f;
-          }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+    mx = halves_max(mx) * a.scale_log2;
+    const bool grow = mx > m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], a.scale_log2, -m_use));
+        rs += p;
+        sacc[kt][r] = p;
       }
+    l_run += rs;
+    if constexpr (DROPOUT) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
+          const Philox4 rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b,
+                                            a.seed_lo, a.seed_hi);
+          if (rnd.x < a.drop_thresh) sacc[kt][4 * g + 0] = 0.f;
+          if (rnd.y < a.drop_thresh) sacc[kt][4 * g + 1] = 0.f;
+          if (rnd.z < a.drop_thresh) sacc[kt][4 * g + 2] = 0.f;
+          if (rnd.w < a.drop_thresh) sacc[kt][4 * g + 3] = 0.f;
+        }
+    }
+    u32x4 pf[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int kt = m >> 1;
+      const int sub = (m & 1) * 8;
+      pf[m] = u32x4{pack2<BF16>(sacc[kt][sub + 0], sacc[kt][sub + 1]),
+                    pack2<BF16>(sacc[kt][sub + 2], sacc[kt][sub + 3]),
+                    pack2<BF16>(sacc[kt][sub + 4], sacc[kt][sub + 5]),
+                    pack2<BF16>(sacc[kt][sub + 6], sacc[kt][sub + 7])};
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-      // ---- O^T += V^T P^T, four 16-key slices
+    // ---- O^T += V^T P^T: the P^T registers are already the B operand (the
+    // key order inside each 16-key slice is permuted and V^T is read with the
+    // same permutation)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int kt = m >> 1;
-        const int sub = (m & 1) * 8;
-        const u32x4 pf = {pack2<BF16>(sacc[kt][sub + 0], sacc[kt][sub + 1]),
-                          pack2<BF16>(sacc[kt][sub + 2], sacc[kt][sub + 3]),
-                          pack2<BF16>(sacc[kt][sub + 4], sacc[kt][sub + 5]),
-                          pack2<BF16>(sacc[kt][sub + 6], sacc[kt][sub + 7])};
-        const int row = 16 * m + 4 * h2 + (sl >> 2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int col = dt * 32 + c0 + 4 * (sl & 3);
-          const u32x2 lo = lds_read_tr(vt_s + T::at(row, col));
-          const u32x2 hi = lds_read_tr(vt_s + T::at(row + 8, col));
-          oacc[dt] = mfma32<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, oacc[dt]);
-        }
-      }
+    for (int j = 0; j < kNO; ++j) {
+      oacc[j % (D / 32)] = mfma32<BF16>(vb[j], pf[j / (D / 32)], oacc[j % (D / 32)]);
+      if (j + kPF < kNO) vb[j + kPF] = vread(j + kPF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kBC;
+    if (t + 1 < ntiles) issue_tile(j0 + kBC, (t & 1) ^ 1);
+    // A wave whose queries all precede the tile has nothing to do in it.
+    if (!CAUSAL || j0 <= qw + 31) {
+      if ((CAUSAL && j0 + kBC - 1 > qw) || j0 + kBC > L)
+        tile(t, std::true_type{});
+      else
+        tile(t, std::false_type{});
     }
     // the next tile's direct loads (issued above) must have landed, and every
     // wave must be done with the current buffers, before the next iteration
