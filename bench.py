@@ -8,9 +8,10 @@ fa_forward (fused tiled forward) followed by the two backward kernels
 (query side: D and dQ; key side: dK and dV), with every input resident in
 HBM.  The
 default workload is the causal B=4, H=8, N=4096, d=128 bf16 configuration.
-W untimed steps run first, then exactly K timed steps bracketed by device
-synchronisation; HIP events on the library's stream time each kernel of every
-step.  Rank 0 prints one JSON line.
+W untimed steps run first (repeated until the GPU clocks have settled, about
+1.5 s), then exactly K timed steps bracketed by device synchronisation; HIP
+events on the library's stream time each kernel of every step.  Rank 0
+prints one JSON line.
 
 Work convention: a visible (query, key) pair costs 4*d flops forward and
 10*d flops backward (B*H*N(N+1)/2 pairs causal, B*H*N^2 otherwise); masked
@@ -94,16 +95,62 @@ def cpu_baseline(wl, x, n_heads: int):
 
 
 def copy_calibration(nbytes: int, steps: int) -> int:
-    """A plain device copy of nbytes, run `steps` times: the reference kernel
-    that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    """A plain elementwise pass over nbytes of fp32 (y = -x: reads nbytes,
+    writes nbytes), run `steps` times: the reference kernel that scales the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
     import torch
     n = nbytes // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(steps):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": steps}), flush=True)
+    print(json.dumps({"calibration_bytes_read": n * 4, "calibration_bytes_written": n * 4, "launches": steps}),
+          flush=True)
+    return 0
+
+
+def _counter_means(csv_path: str, counter: str):
+    """Mean value of a counter per kernel name over the dispatches of a
+    rocprofv3 counter_collection.csv."""
+    import csv
+    import re
+    acc = {}
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            m = re.search(r"(fa_\w+_kernel)", row["Kernel_Name"])
+            name = m.group(1) if m else row["Kernel_Name"]
+            acc.setdefault(name, {})
+            acc[name][row["Dispatch_Id"]] = acc[name].get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+
+
+def pmc_summary(pmc_dir: str, calib_bytes: int) -> int:
+    """Turn four rocprofv3 --pmc runs (fetch/, write/: this benchmark;
+    calib_fetch/, calib_write/: the calibration pass of calib_bytes) into
+    per-launch HBM traffic of each kernel, written to TRAFFIC_FILE together
+    with the hash of the kernel sources it was measured on."""
+    f = _counter_means(os.path.join(pmc_dir, "fetch", "run_counter_collection.csv"), "FETCH_SIZE")
+    w = _counter_means(os.path.join(pmc_dir, "write", "run_counter_collection.csv"), "WRITE_SIZE")
+    cf = _counter_means(os.path.join(pmc_dir, "calib_fetch", "run_counter_collection.csv"), "FETCH_SIZE")
+    cw = _counter_means(os.path.join(pmc_dir, "calib_write", "run_counter_collection.csv"), "WRITE_SIZE")
+    # the calibration kernel is the launch with the largest fetch
+    calib = max(cf, key=cf.get)
+    fetch_scale = calib_bytes / cf[calib]
+    write_scale = calib_bytes / cw[calib]
+    out = {"calibration": {"kernel": calib, "bytes": calib_bytes, "FETCH_SIZE": cf[calib], "WRITE_SIZE": cw[calib],
+                           "fetch_bytes_per_unit": fetch_scale, "write_bytes_per_unit": write_scale}}
+    for k in KERNEL_SOURCES:
+        if k in f and k in w:
+            out[k] = {"FETCH_SIZE": f[k], "WRITE_SIZE": w[k], "fetch_bytes": f[k] * fetch_scale,
+                      "write_bytes": w[k] * write_scale, "traffic_bytes": f[k] * fetch_scale + w[k] * write_scale,
+                      "source_sha256": kernel_source_hash(k)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
     return 0
 
 
@@ -114,9 +161,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index (3 = the causal headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8,
+    ap.add_argument("--cpu-heads", type=int, default=32,
                     help="oracle sample size in (batch, head) pairs (about 10-30 s of host work); 0 = all")
-    ap.add_argument("--copy-bytes", type=int, default=0, help="run only the copy-kernel counter calibration")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="run only the counter calibration pass over this many bytes")
+    ap.add_argument("--pmc-summary", default="", help="directory of rocprofv3 --pmc runs to turn into the traffic file")
+    ap.add_argument("--calib-bytes", type=int, default=1 << 30, help="bytes of the calibration pass of --pmc-summary")
+    ap.add_argument("--settle-s", type=float, default=1.5,
+                    help="repeat the warm-up steps until this many seconds have passed (clock settling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels shard by (batch, head) "
@@ -125,6 +176,8 @@ def main() -> int:
 
     if args.copy_bytes:
         return copy_calibration(args.copy_bytes, args.steps)
+    if args.pmc_summary:
+        return pmc_summary(args.pmc_summary, args.calib_bytes)
 
     import torch
     import exact_tiled_attention_40_amd as fa
@@ -159,9 +212,16 @@ def main() -> int:
             fa.fa_backward_stage(s, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream, **kw)
             if ev: ev[2 + s].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # W warm-up steps, repeated until at least --settle-s seconds have passed:
+    # the GPU clocks take about a second of load to settle, and a step is
+    # under a millisecond.
+    t_settle = time.perf_counter()
+    while True:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_settle >= args.settle_s or args.warmup == 0:
+            break
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
