@@ -1,13 +1,13 @@
 #!/usr/bin/env python3
 """Attention forward + backward throughput on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 fa_forward (fused tiled forward) followed by the two backward kernels
 (query side: D and dQ; key side: dK and dV), with every input resident in
 HBM.  The
-default workload is the causal B=4, H=8, N=4096, d=128 bf16 configuration.
+default workload is the causal B=4, H=8, N=4096, d=128 bf16 one.
 W untimed steps run first (repeated until the GPU clocks have settled, about
 1.5 s), then exactly K timed steps bracketed by device synchronisation; HIP
 events on the library's stream time each kernel of every step.  Rank 0
@@ -159,7 +159,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload index (3 = the causal headline)")
+    ap.add_argument("--workload", default=None, help="workload name (default: the causal B4 H8 N4096 d128 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="oracle sample size in (batch, head) pairs (about 10-30 s of host work); 0 = all")
@@ -183,7 +183,7 @@ def main() -> int:
     import exact_tiled_attention_40_amd as fa
     import workloads
 
-    wl = workloads.CONFIGS[args.config]
+    wl = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
     if wl.varlen:
         print("bench.py times the fixed-length workloads", file=sys.stderr)
         return 2

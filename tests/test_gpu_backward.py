@@ -96,8 +96,12 @@ def test_backward_writes_only_its_outputs():
         assert (b[:2048] == 7.0).all() and (b[2048 + n:] == 7.0).all()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_backward_config(cfg):
-    x = workloads.make_inputs(workloads.CONFIGS[cfg])
-    n_heads = {1: None, 2: 4, 3: 3, 4: 2, 5: 3}[cfg]
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_backward_workload(name):
+    # every head of the small workloads; a seeded sample of (sequence, head)
+    # pairs, always including the first and the last, of the large ones
+    x = workloads.make_inputs(workloads.WORKLOADS[name])
+    n_heads = {"tiny_B1_H2_N128_d64_f16": None, "packed_qkv_B2_H12_N2048_d64_f16": 4,
+               "causal_B4_H8_N4096_d128_bf16": 3, "long_causal_B1_H16_N8192_d128_bf16_kx4": 2,
+               "varlen16_H32_d128_bf16_causal_p0.1": 3}[name]
     check(x, n_heads)

@@ -3,12 +3,12 @@
 This module only draws random numbers; it holds none of the attention
 arithmetic, so both the oracle-side tests and the GPU path can use it.
 
-Recipe (all configurations): a CPU ``torch.Generator`` seeded with
-``1000 + config index`` draws, in this order, [the varlen sequence lengths],
-q, k, v, dO as float32 standard normals, each rounded once (round to nearest
-even) to the configuration's dtype.  The long-sequence configuration then
-multiplies the rounded K by 4 (exact in fp16 and bf16).  The packed-QKV
-configuration draws q, k and v together as one [B, N, 3, H, d] tensor and
+Recipe (every workload): a CPU ``torch.Generator`` seeded with the
+workload's seed draws, in this order, [the varlen sequence lengths], q, k, v,
+dO as float32 standard normals, each rounded once (round to nearest even) to
+the workload's dtype.  The long-sequence workload then multiplies the
+rounded K by 4 (exact in fp16 and bf16).  The packed-QKV workload draws q, k
+and v together as one [B, N, 3, H, d] tensor and
 uses views into it.  Varlen lengths are discrete uniform on [128, 4096],
 both ends included.
 
@@ -52,17 +52,19 @@ class Workload:
         return 1.0 / math.sqrt(self.d)
 
 
-CONFIGS = {
-    1: Workload("tiny_B1_H2_N128_d64_f16", 1, 2, 128, 64, "f16", False, seed=1001),
-    2: Workload("packed_qkv_B2_H12_N2048_d64_f16", 2, 12, 2048, 64, "f16", False, packed=True, seed=1002),
-    3: Workload("causal_B4_H8_N4096_d128_bf16", 4, 8, 4096, 128, "bf16", True, seed=1003),
-    4: Workload("long_causal_B1_H16_N8192_d128_bf16_kx4", 1, 16, 8192, 128, "bf16", True, k_mult=4.0,
-                seed=1004),
-    5: Workload("varlen16_H32_d128_bf16_causal_p0.1", 16, 32, 4096, 128, "bf16", True, dropout_p=0.1,
-                varlen=True, seed=1005),
-}
+# The five workloads, by name; the seed of each is fixed (1001 .. 1005).
+WORKLOADS = {w.name: w for w in (
+    Workload("tiny_B1_H2_N128_d64_f16", 1, 2, 128, 64, "f16", False, seed=1001),
+    Workload("packed_qkv_B2_H12_N2048_d64_f16", 2, 12, 2048, 64, "f16", False, packed=True, seed=1002),
+    Workload("causal_B4_H8_N4096_d128_bf16", 4, 8, 4096, 128, "bf16", True, seed=1003),
+    Workload("long_causal_B1_H16_N8192_d128_bf16_kx4", 1, 16, 8192, 128, "bf16", True, k_mult=4.0,
+             seed=1004),
+    Workload("varlen16_H32_d128_bf16_causal_p0.1", 16, 32, 4096, 128, "bf16", True, dropout_p=0.1,
+             varlen=True, seed=1005),
+)}
 
-HEADLINE = 3
+# the workload the benchmark times: causal B=4, H=8, N=4096, d=128, bf16
+HEADLINE = "causal_B4_H8_N4096_d128_bf16"
 
 
 @dataclasses.dataclass
