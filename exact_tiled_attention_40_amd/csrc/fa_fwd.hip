@@ -124,18 +124,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   }
 
   const uint32_t ks0 = lds_addr(ks), vs0 = lds_addr(vs);
-  // Direct HBM -> LDS tile load: wave w issues blocks w, w + kWaves, ... of
-  // each tensor's tile.
-  auto issue_tile = [&](int j0, int buf) {
+  // Direct HBM -> LDS loads of one K or V tile: wave w issues blocks w,
+  // w + kWaves, ... of it.
+  auto issue = [&](const uint16_t* base, uint32_t lds, int j0) {
     const int rows = min(kBC, L - j0);
     const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)j0 * ld, bytes);
 #pragma unroll
-    for (int u = 0; u < T::kBlocks / kWaves; ++u) {
-      T::load(kr, ks0 + buf * T::kBytes, row_bytes, u * kWaves + w, lane);
-      T::load(vr, vs0 + buf * T::kBytes, row_bytes, u * kWaves + w, lane);
-    }
+    for (int u = 0; u < T::kBlocks / kWaves; ++u) T::load(r, lds, row_bytes, u * kWaves + w, lane);
   };
 
   f32x16 oacc[D / 32];
@@ -143,37 +139,26 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY;  // reference max, in units of log2 (scores * scale * log2 e)
   float l_run = 0.f;        // this lane's share of the row sum
+  f32x16 sacc[2];           // S^T of the tile being prepared (two 32-key halves)
+  u32x4 pf[4];              // P^T of the tile being accumulated, as B operands
 
   const uint32_t ob0 = T::opnd_base(lane, 0), ob1 = T::opnd_base(lane, 1);
   const uint32_t tb0 = T::tr_base(lane, 0), tb1 = T::tr_base(lane, 1);
 
-  issue_tile(0, 0);
-  wait_vmem();
-  __syncthreads();
+  // Last tile this wave needs: causal waves stop at the tile holding their
+  // last query; waves that start past a ragged end need none.
+  const int last = qw >= L ? -1 : (CAUSAL ? min(ntiles - 1, (qw + 31) / kBC) : ntiles - 1);
 
-  // One tile of 64 keys.  Instruction order (sched_barrier fences keep it):
-  // the S^T products with their K operands read kPF products ahead; the first
-  // V^T transpose reads; the softmax; the O^T products with their V^T
-  // operands read kPF products ahead.
-  auto tile = [&](int t, auto mask_tag) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    const int cur = t & 1;
-    const int j0 = t * kBC;
-    uint32_t k0 = ks0 + cur * T::kBytes + ob0, k1 = ks0 + cur * T::kBytes + ob1;
-    uint32_t v0 = vs0 + cur * T::kBytes + tb0, v1 = vs0 + cur * T::kBytes + tb1;
-    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
-    auto kread = [&](int i) {  // product i: key tile i & 1, k-step i >> 1
+  // S^T = K Q^T of tile t into sacc, K operands read kPF products ahead.
+  auto s_products = [&](int t) {
+    uint32_t k0 = ks0 + (t & 1) * T::kBytes + ob0, k1 = ks0 + (t & 1) * T::kBytes + ob1;
+    asm volatile("" : "+v"(k0), "+v"(k1));
+    auto kread = [&](int i) {  // product i: key half i & 1, k-step i >> 1
       const int s = i >> 1;
       return lds_read16_at(((s & 1) ? k1 : k0) + T::opnd_off(i & 1, s));
     };
-    auto vread = [&](int j) {  // product j: key slice j / (D/32), head-dim tile j % (D/32)
-      const uint32_t o = T::tr_off(j / (D / 32), j % (D / 32));
-      const u32x2 lo = lds_read_tr_at(v0 + o), hi = lds_read_tr_at(v1 + o);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
-
-    // ---- S^T = K Q^T for keys j0 .. j0+63
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
     u32x4 kb[kNS];
 #pragma unroll
     for (int i = 0; i < kPF; ++i) kb[i] = kread(i);
@@ -184,13 +169,80 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
       if (i + kPF < kNS) kb[i + kPF] = kread(i + kPF);
       __builtin_amdgcn_sched_barrier(0);
     }
-    u32x4 vb[kNO];
-#pragma unroll
-    for (int j = 0; j < kPF; ++j) vb[j] = vread(j);
+  };
 
-    // ---- mask keys after the query (causal) and beyond the sequence end;
-    // register r of key tile kt holds key j0 + kt*32 + 8*(r/4) + 4*h2 + r%4
-    if constexpr (kMask) {
+  // Matrix phase of tile t: O^T += V^T P^T of tile t (if the wave needs it)
+  // interleaved with S^T of tile t + 1 (if needed), LDS operands read kPF
+  // products ahead.  The P^T registers are already the B operand (the key
+  // order inside each 16-key slice is permuted and V^T is read with the
+  // same permutation).
+  auto m_phase = [&](int t) {
+    const bool do_pv = t <= last, do_s = t + 1 <= last;
+    if (do_pv && do_s) {
+      uint32_t k0 = ks0 + ((t + 1) & 1) * T::kBytes + ob0, k1 = ks0 + ((t + 1) & 1) * T::kBytes + ob1;
+      uint32_t v0 = vs0 + (t & 1) * T::kBytes + tb0, v1 = vs0 + (t & 1) * T::kBytes + tb1;
+      asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
+      auto kread = [&](int i) {
+        const int s = i >> 1;
+        return lds_read16_at(((s & 1) ? k1 : k0) + T::opnd_off(i & 1, s));
+      };
+      auto vread = [&](int j) {  // product j: key slice j / (D/32), head-dim tile j % (D/32)
+        const uint32_t o = T::tr_off(j / (D / 32), j % (D / 32));
+        const u32x2 lo = lds_read_tr_at(v0 + o), hi = lds_read_tr_at(v1 + o);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      static_assert(kNS == kNO, "the two product streams are interleaved one to one");
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+      u32x4 kb[kNS], vb[kNO];
+#pragma unroll
+      for (int i = 0; i < kPF; ++i) {
+        vb[i] = vread(i);
+        kb[i] = kread(i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kNS; ++i) {
+        oacc[i % (D / 32)] = mfma32<BF16>(vb[i], pf[i / (D / 32)], oacc[i % (D / 32)]);
+        if (i & 1)
+          s1 = mfma32<BF16>(kb[i], qf[i >> 1], s1);
+        else
+          s0 = mfma32<BF16>(kb[i], qf[i >> 1], s0);
+        if (i + kPF < kNS) {
+          vb[i + kPF] = vread(i + kPF);
+          kb[i + kPF] = kread(i + kPF);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sacc[0] = s0;
+      sacc[1] = s1;
+    } else if (do_pv) {
+      uint32_t v0 = vs0 + (t & 1) * T::kBytes + tb0, v1 = vs0 + (t & 1) * T::kBytes + tb1;
+      asm volatile("" : "+v"(v0), "+v"(v1));
+      auto vread = [&](int j) {
+        const uint32_t o = T::tr_off(j / (D / 32), j % (D / 32));
+        const u32x2 lo = lds_read_tr_at(v0 + o), hi = lds_read_tr_at(v1 + o);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4 vb[kNO];
+#pragma unroll
+      for (int j = 0; j < kPF; ++j) vb[j] = vread(j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kNO; ++j) {
+        oacc[j % (D / 32)] = mfma32<BF16>(vb[j], pf[j / (D / 32)], oacc[j % (D / 32)]);
+        if (j + kPF < kNO) vb[j + kPF] = vread(j + kPF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Vector phase of tile t: mask, online softmax of sacc (register r of key
+  // half kt holds key t*kBC + kt*32 + 8*(r/4) + 4*h2 + r%4), dropout, and the
+  // P^T operands of the next matrix phase.
+  auto v_phase = [&](int t) {
+    if (t > last) return;
+    const int j0 = t * kBC;
+    if ((CAUSAL && j0 + kBC - 1 > qw) || j0 + kBC > L) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -199,7 +251,6 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
           if ((CAUSAL && kj > qi) || kj >= L) sacc[kt][r] = -INFINITY;
         }
     }
-    // ---- online softmax with a lazily rescaled reference max
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -208,6 +259,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
     mx = halves_max(mx) * a.scale_log2;
     const bool grow = mx > m_run + kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      // rare: keep it a branch (the compiler would otherwise speculate the
+      // rescale of the whole accumulator into every tile)
+      asm volatile("" ::: "memory");
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
       m_run = grow ? mx : m_run;
       l_run *= alpha;
@@ -239,7 +293,6 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
           if (rnd.w < a.drop_thresh) sacc[kt][4 * g + 3] = 0.f;
         }
     }
-    u32x4 pf[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int kt = m >> 1;
@@ -249,34 +302,42 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
                     pack2<BF16>(sacc[kt][sub + 4], sacc[kt][sub + 5]),
                     pack2<BF16>(sacc[kt][sub + 6], sacc[kt][sub + 7])};
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- O^T += V^T P^T: the P^T registers are already the B operand (the
-    // key order inside each 16-key slice is permuted and V^T is read with the
-    // same permutation)
-#pragma unroll
-    for (int j = 0; j < kNO; ++j) {
-      oacc[j % (D / 32)] = mfma32<BF16>(vb[j], pf[j / (D / 32)], oacc[j % (D / 32)]);
-      if (j + kPF < kNO) vb[j + kPF] = vread(j + kPF);
-      __builtin_amdgcn_sched_barrier(0);
-    }
   };
 
+  // Two groups of four waves (one wave of each per SIMD) alternate a vector
+  // phase V(t) (softmax of tile t) with a matrix phase M(t) (PV of tile t,
+  // S of tile t + 1); the second group runs one phase behind the first, so
+  // that on every SIMD one wave issues matrix products while the other does
+  // its softmax.  Slots are separated by workgroup barriers: group 0 runs
+  // V(t) in slot 2t and M(t) in slot 2t + 1, group 1 one slot later.  K and V
+  // tiles are double-buffered (K(t), V(t) in buffer t % 2): K(t+2) and V(t+1)
+  // are issued at the start of slot 2t + 1 (their buffers were last read in
+  // slot 2t) and waited for at the end of slot 2t + 2.
+  issue(kbase, ks0, 0);
+  issue(vbase, vs0, 0);
+  if (ntiles > 1) issue(kbase, ks0 + T::kBytes, kBC);
+  wait_vmem();
+  __syncthreads();
+  const int grp = w / (kWaves / 2);
+  auto issue_next = [&](int t) {  // the loads of slot 2t + 1
+    if (t + 2 < ntiles) issue(kbase, ks0 + (t & 1) * T::kBytes, (t + 2) * kBC);
+    if (t + 1 < ntiles) issue(vbase, vs0 + ((t + 1) & 1) * T::kBytes, (t + 1) * kBC);
+  };
+  if (last >= 0) s_products(0);
+  if (grp == 1) __syncthreads();  // slot 0: group 1 idle
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kBC;
-    if (t + 1 < ntiles) issue_tile(j0 + kBC, (t & 1) ^ 1);
-    // A wave whose queries all precede the tile has nothing to do in it.
-    if (!CAUSAL || j0 <= qw + 31) {
-      if ((CAUSAL && j0 + kBC - 1 > qw) || j0 + kBC > L)
-        tile(t, std::true_type{});
-      else
-        tile(t, std::false_type{});
-    }
-    // the next tile's direct loads (issued above) must have landed, and every
-    // wave must be done with the current buffers, before the next iteration
-    wait_vmem();
+    // V(t): slot 2t + grp
+    if (grp == 1) issue_next(t);
+    v_phase(t);
+    if (grp == 0 && t > 0) wait_vmem();
+    __syncthreads();
+    // M(t): slot 2t + 1 + grp
+    if (grp == 0) issue_next(t);
+    m_phase(t);
+    if (grp == 1) wait_vmem();
     __syncthreads();
   }
+  if (grp == 0) __syncthreads();  // slot 2 * ntiles: group 0 idle
 
   // ---- epilogue
   const float l_tot = halves_sum(l_run);
