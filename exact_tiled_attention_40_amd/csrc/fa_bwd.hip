@@ -393,13 +393,16 @@ __device__ __forceinline__ f32x4 lds_f32x4(uint32_t addr) {
 //            products ahead), with elements 0..7 of the next half computed
 //            between them once its S, dP are complete.
 // Either phase then carries about three VALU instructions per product, few
-// enough for the wave to issue them while its products run.  On return
-// sacc, pacc, zpk[0..3], spk[0..3] describe the next half.
-template <int D, bool BF16, bool MASK, bool DROPOUT>
+// enough for the wave to issue them while its products run.  hook(i) runs
+// after look-ahead product i (the caller issues its tile loads there, so that
+// their issue overlaps the products).  On return sacc, pacc, zpk[0..3],
+// spk[0..3] describe the next half.
+template <int D, bool BF16, bool MASK, bool DROPOUT, typename Hook>
 __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st, f32x16& sacc, f32x16& pacc,
                                           uint32_t (&zpk)[8], uint32_t (&spk)[8], u32x4 (&pf)[4],
                                           const TileAddr& nop, const TileAddr& nnop, int nnqt, const TileAddr& tr,
-                                          const HalfCtx& cur, const HalfCtx& nxt, int kj, int h2, int b, int h) {
+                                          const HalfCtx& cur, const HalfCtx& nxt, int kj, int h2, int b, int h,
+                                          Hook&& hook) {
   using T = MTile<D, kBR>;
   constexpr int kNP = D / 8;  // look-ahead products (S and dP, D/16 k-steps each)
   constexpr int kPF = 4;      // LDS operand reads in flight (products ahead)
@@ -442,6 +445,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
       ob[i + kPF] = opnd(nop, nxt.qt, i + kPF);
     else
       tb[i + kPF - kNP] = tr_pair(i + kPF - kNP);
+    hook(i);  // work the caller spreads over the products (tile loads)
 #pragma unroll
     for (int r = 8 + (i * 8) / kNP; r < 8 + ((i + 1) * 8) / kNP; ++r) {
       const f32x4& l4 = r < 12 ? l4a : l4b;
@@ -513,6 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t gs[kNB][T::kElems];
   __shared__ __attribute__((aligned(16))) float ls[kNB][kBR];
   __shared__ __attribute__((aligned(16))) float dls[kNB][kBR];
+  __shared__ __attribute__((aligned(16))) float spare[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -579,6 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const float* lbase = a.lse2 + (int64_t)start * a.H + h;
   const float* dbase = a.delta + (int64_t)start * a.H + h;
   const uint32_t qs0 = lds_addr(qs), gs0 = lds_addr(gs), ls0 = lds_addr(ls), dls0 = lds_addr(dls);
+  const uint32_t hstride4 = (uint32_t)a.H * 4;  // bytes between consecutive tokens of LSE and D
 
   auto issue_tile = [&](int i0, int buf) {
     const int rows = min(kBR, L - i0);
@@ -646,7 +652,37 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     // (the reads still in flight here touch tiles t and t + 1 only)
     wait_vmem();
     barrier_keep_lds_reads();
-    if (t + 2 < ntiles) issue_tile(i0 + 2 * kBR, (t + 2) % kNB);
+
+    // Loads of tile t + 2 into buffer (t + 2) % kNB, spread over the first
+    // half's look-ahead products: Q and dO blocks at even products, LSE or D
+    // (waves 0 and 1) at product 1.  Past the last tile the buffer ranges
+    // are empty: the loads fetch nothing and fill the free buffer with zeros.
+    const int i2 = i0 + 2 * kBR;
+    const int rows = t + 2 < ntiles ? min(kBR, L - i2) : 0;
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(qbase + (int64_t)min(i2, L - 1) * ld, rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u);
+    const __amdgpu_buffer_rsrc_t gr =
+        make_rsrc(gbase + (int64_t)min(i2, L - 1) * hd, rows > 0 ? (uint32_t)(rows - 1) * grow_bytes + D * 2 : 0u);
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc((w == 0 ? lbase : dbase) + (int64_t)min(i2, L - 1) * a.H,
+                  rows > 0 ? (uint32_t)(rows - 1) * a.H * 4 + 4 : 0u);
+    const int lbuf = (t + 2) % kNB;
+    // waves 2 and 3 send their (empty) LSE/D load to a spare row
+    const uint32_t xdst = w == 0 ? ls0 + lbuf * kBR * 4 : w == 1 ? dls0 + lbuf * kBR * 4 : lds_addr(spare);
+    const uint32_t qdst = qs0 + lbuf * T::kBytes, gdst = gs0 + lbuf * T::kBytes;
+    const uint32_t xoff = (uint32_t)lane * hstride4;
+    auto load_hook = [=](int i) {
+      constexpr int kNU = T::kBlocks / kWaves;  // blocks per tensor per wave
+      if (i % 2 == 0 && i / 2 < 2 * kNU) {
+        const int k = i / 2;
+        if (k & 1)
+          T::load(gr, gdst, grow_bytes, (k >> 1) * kWaves + w, lane);
+        else
+          T::load(qr, qdst, row_bytes, (k >> 1) * kWaves + w, lane);
+      }
+      if (i == 1) buffer_load_lds4_addr(w < 2 ? xr : make_rsrc(nullptr, 0u), xdst, xoff);
+    };
+    auto no_hook = [](int) {};
 
     const uint32_t qb = qs0 + buf * T::kBytes, gb = gs0 + buf * T::kBytes;
     const uint32_t nqb = qs0 + nbuf * T::kBytes, ngb = gs0 + nbuf * T::kBytes;
@@ -660,8 +696,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     // discarded; doing it anyway keeps the tile one basic block.  Masked
     // tiles come first, so the look-ahead into the next tile may use this
     // tile's masking.
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj, h2, b, h);
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2, b, h);
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj, h2, b, h,
+                                       load_hook);
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2, b, h,
+                                       no_hook);
   };
   // Causal: only the first two tiles (queries j0 .. j0+127) hold queries
   // before some key of the block, so only they are masked.

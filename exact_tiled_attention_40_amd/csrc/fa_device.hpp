@@ -171,6 +171,31 @@ __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// buffer_load_lds4 with the LDS destination given as a byte address.
+__device__ __forceinline__ void buffer_load_lds4_addr(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voffset) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voffset), "s"(r)
+      : "memory");
+}
+
+// Direct HBM -> LDS loads through the compiler builtin (it sets M0 itself):
+// every lane's 16 (or 4) bytes land at lds + 16*lane (4*lane).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voffset,
+                                           0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 4, voffset,
+                                           0, 0, 0);
+}
+
 // A tile of ROWS rows (a multiple of 32) of D 16-bit elements in LDS, laid
 // out for the two ways the MFMA loops read it:
 //   - operand read: lane l of a wave takes the 16-byte chunk 2s + l/32 of row
