@@ -64,6 +64,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   constexpr int kNS = 2 * (D / 16);  // S^T products per tile (two 32-key tiles x D/16 k-steps)
   constexpr int kNO = 4 * (D / 32);  // O^T products per tile (four 16-key slices x D/32 tiles)
   constexpr int kPF = 4;             // LDS operand reads in flight (products ahead)
+  constexpr int kLoads = 2 * (T::kBlocks / kWaves);  // 1 KB tile loads per wave per tile step
+  static_assert(kLoads == 2 || kLoads == 4, "load spreading assumes 2 or 4 loads per step");
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
 
@@ -176,9 +178,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   // products ahead.  The P^T registers are already the B operand (the key
   // order inside each 16-key slice is permuted and V^T is read with the
   // same permutation).
-  auto m_phase = [&](int t) {
-    const bool do_pv = t <= last, do_s = t + 1 <= last;
-    if (do_pv && do_s) {
+  auto m_phase = [&](int t, bool do_s, auto&& hook) __attribute__((always_inline)) {
+    if (do_s) {
       uint32_t k0 = ks0 + ((t + 1) & 1) * T::kBytes + ob0, k1 = ks0 + ((t + 1) & 1) * T::kBytes + ob1;
       uint32_t v0 = vs0 + (t & 1) * T::kBytes + tb0, v1 = vs0 + (t & 1) * T::kBytes + tb1;
       asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
@@ -211,11 +212,12 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
           vb[i + kPF] = vread(i + kPF);
           kb[i + kPF] = kread(i + kPF);
         }
+        if (i % (kNS / kLoads) == 1) hook(i / (kNS / kLoads));
         __builtin_amdgcn_sched_barrier(0);
       }
       sacc[0] = s0;
       sacc[1] = s1;
-    } else if (do_pv) {
+    } else {
       uint32_t v0 = vs0 + (t & 1) * T::kBytes + tb0, v1 = vs0 + (t & 1) * T::kBytes + tb1;
       asm volatile("" : "+v"(v0), "+v"(v1));
       auto vread = [&](int j) {
@@ -239,10 +241,15 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   // Vector phase of tile t: mask, online softmax of sacc (register r of key
   // half kt holds key t*kBC + kt*32 + 8*(r/4) + 4*h2 + r%4), dropout, and the
   // P^T operands of the next matrix phase.
-  auto v_phase = [&](int t) {
-    if (t > last) return;
+  auto v_phase = [&](int t, bool may_mask, auto&& hook) __attribute__((always_inline)) {
+    // hook(u) for each of the kLoads tile loads, spread over four points
+    auto at = [&](int point) {
+      if constexpr (kLoads == 4) hook(point);
+      else if (point % 2 == 0) hook(point / 2);
+    };
+    at(0);
     const int j0 = t * kBC;
-    if ((CAUSAL && j0 + kBC - 1 > qw) || j0 + kBC > L) {
+    if (may_mask && ((CAUSAL && j0 + kBC - 1 > qw) || j0 + kBC > L)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -257,6 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
     mx = halves_max(mx) * a.scale_log2;
+    at(1);
     const bool grow = mx > m_run + kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       // rare: keep it a branch (the compiler would otherwise speculate the
@@ -271,13 +279,15 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], a.scale_log2, -m_use));
         rs += p;
         sacc[kt][r] = p;
       }
+      at(2 + kt);
+    }
     l_run += rs;
     if constexpr (DROPOUT) {
 #pragma unroll
@@ -319,25 +329,63 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   wait_vmem();
   __syncthreads();
   const int grp = w / (kWaves / 2);
-  auto issue_next = [&](int t) {  // the loads of slot 2t + 1
-    if (t + 2 < ntiles) issue(kbase, ks0 + (t & 1) * T::kBytes, (t + 2) * kBC);
-    if (t + 1 < ntiles) issue(vbase, vs0 + ((t + 1) & 1) * T::kBytes, (t + 1) * kBC);
+  // Load u (0 <= u < kLoads) of this wave's share of slot 2t + 1: blocks of
+  // K(t+2) into buffer t % 2, then of V(t+1) into buffer (t+1) % 2 (both
+  // buffers were last read in slot 2t).
+  auto load_part = [&](int t, int u) __attribute__((always_inline)) {
+    constexpr int per = T::kBlocks / kWaves;
+    const bool isk = u < per;
+    const int tt = isk ? t + 2 : t + 1;
+    if (tt >= ntiles) return;
+    const int j0 = tt * kBC;
+    const uint32_t bytes = (uint32_t)(min(kBC, L - j0) - 1) * row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((isk ? kbase : vbase) + (int64_t)j0 * ld, bytes);
+    const uint32_t lds = isk ? ks0 + (t & 1) * T::kBytes : vs0 + ((t + 1) & 1) * T::kBytes;
+    T::load(r, lds, row_bytes, (isk ? u : u - per) * kWaves + w, lane);
   };
-  if (last >= 0) s_products(0);
-  if (grp == 1) __syncthreads();  // slot 0: group 1 idle
-  for (int t = 0; t < ntiles; ++t) {
-    // V(t): slot 2t + grp
-    if (grp == 1) issue_next(t);
-    v_phase(t);
-    if (grp == 0 && t > 0) wait_vmem();
-    __syncthreads();
-    // M(t): slot 2t + 1 + grp
-    if (grp == 0) issue_next(t);
-    m_phase(t);
-    if (grp == 1) wait_vmem();
-    __syncthreads();
-  }
-  if (grp == 0) __syncthreads();  // slot 2 * ntiles: group 0 idle
+  auto no_hook = [](int) {};
+  // The loop for one group G, whose wave-level schedule is fixed at compile
+  // time: group 0 spreads its loads of slot 2t + 1 between the products of
+  // M(t), group 1 through the softmax of V(t), so that no wave stalls on a
+  // burst of load issues.
+  auto run = [&](auto G) __attribute__((always_inline)) {
+    constexpr int g = decltype(G)::value;
+    if (last >= 0) s_products(0);
+    if (g == 1) __syncthreads();  // slot 0: group 1 idle
+    // Only the wave's last tile can hold masked keys (causal diagonal or the
+    // ragged end), so the tiles before it run without mask code.
+    int t = 0;
+    for (; t < last; ++t) {
+      auto loads = [&](int u) { load_part(t, u); };
+      if constexpr (g == 1) v_phase(t, false, loads);
+      else v_phase(t, false, no_hook);
+      if (g == 0 && t > 0) wait_vmem();
+      __syncthreads();
+      if constexpr (g == 0) m_phase(t, true, loads);
+      else m_phase(t, true, no_hook);
+      if (g == 1) wait_vmem();
+      __syncthreads();
+    }
+    // The wave's last tile, then the slots of tiles it does not need (it
+    // still issues its share of their loads).
+    for (; t < ntiles; ++t) {
+      if (g == 1)
+        for (int u = 0; u < kLoads; ++u) load_part(t, u);
+      if (t == last) v_phase(t, true, no_hook);
+      if (g == 0 && t > 0) wait_vmem();
+      __syncthreads();
+      if (g == 0)
+        for (int u = 0; u < kLoads; ++u) load_part(t, u);
+      if (t == last) m_phase(t, false, no_hook);
+      if (g == 1) wait_vmem();
+      __syncthreads();
+    }
+    if (g == 0) __syncthreads();  // slot 2 * ntiles: group 0 idle
+  };
+  if (grp == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
 
   // ---- epilogue
   const float l_tot = halves_sum(l_run);
