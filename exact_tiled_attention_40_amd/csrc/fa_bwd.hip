@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   // interleaved, their K/V operands read kPF products ahead; the first K^T
   // transpose reads; P and dS; dQ^T += K^T dS^T with its K^T operands read
   // kPF products ahead.
-  auto tile = [&](int t, auto mask_tag) {
+  auto tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     const int cur = t & 1;
     const int j0 = t * kBC;
@@ -282,16 +282,22 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kBC;
-    if (t + 1 < ntiles) issue_tile(j0 + kBC, (t & 1) ^ 1);
-    // a wave whose queries all precede the tile has nothing to do in it
-    if (!CAUSAL || j0 <= qw + 31) {
-      if ((CAUSAL && j0 + kBC - 1 > qw) || j0 + kBC > L)
-        tile(t, std::true_type{});
-      else
-        tile(t, std::false_type{});
-    }
+  // Last tile this wave needs (its queries all precede the later ones; a
+  // wave past a ragged end needs none).  Only that tile can hold masked keys
+  // (causal diagonal or the ragged end), so the tiles before it run without
+  // mask code, and the loop keeps one accumulator path.  Every wave still
+  // issues its share of every tile load and joins every barrier.
+  const int last = qw >= L ? -1 : (CAUSAL ? min(ntiles - 1, (qw + 31) / kBC) : ntiles - 1);
+  int t = 0;
+  for (; t < last; ++t) {
+    if (t + 1 < ntiles) issue_tile((t + 1) * kBC, (t & 1) ^ 1);
+    tile(t, std::false_type{});
+    wait_vmem();
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue_tile((t + 1) * kBC, (t & 1) ^ 1);
+    if (t == last) tile(t, std::true_type{});
     wait_vmem();
     __syncthreads();
   }
