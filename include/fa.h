@@ -91,9 +91,10 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int dtype, int64_t ld_qkv);
 
 /* Bytes of device workspace fa_backward needs for B sequences of at most N
- * tokens with H heads of size d: the fp32 row terms D = rowsum(dO * O)
- * [B*N, H].  Returns 0 if the size overflows.  Host-only, never fails
- * otherwise. */
+ * tokens with H heads of size d: two fp32 [B*N, H] arrays, each rounded up
+ * to 256 bytes, the row terms D = rowsum(dO * O) and lse * log2(e) (written
+ * by the query-side kernel, read by the key-side kernel).  Returns 0 if the
+ * size overflows.  Host-only, never fails otherwise. */
 size_t fa_backward_workspace_size(int B, int N, int H, int d);
 
 /* Backward pass (recomputation from lse, lab write-up section 3.3).
