@@ -344,20 +344,46 @@ __device__ __forceinline__ TileAddr tile_addr(uint32_t qb, uint32_t gb, uint32_t
   return t;
 }
 
+// 32x32x16 product accumulated in place in VGPRs (inline assembly, so the
+// result stays in VGPRs even where the compiler keeps its own products in
+// AGPRs).  The compiler does not see these as matrix products: a VALU read
+// of the result must come at least 19 wait states after the product
+// (mfma_vgpr_wait), which the callers guarantee.
+template <bool BF16>
+__device__ __forceinline__ void mfma32_v(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+template <bool BF16>
+__device__ __forceinline__ void mfma32_v0(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory"); }
+
 // S = Q K^T and dP = dO V^T for queries 32qt .. 32qt+31 of a tile (pipeline
 // prologue only; the loop computes them inside dkdv_half).
 template <int D, bool BF16>
 __device__ __forceinline__ void dkdv_sdp(const KVState<D, BF16>& st, const TileAddr& op, int qt, f32x16& sacc,
                                          f32x16& pacc) {
   using T = MTile<D, kBR>;
-  sacc = f32x16{};
-  pacc = f32x16{};
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const uint32_t qa = (s & 1) ? op.q1 : op.q0, ga = (s & 1) ? op.g1 : op.g0;
-    sacc = mfma32<BF16>(lds_read16_at(qa + T::opnd_off(qt, s)), st.kf[s], sacc);
-    pacc = mfma32<BF16>(lds_read16_at(ga + T::opnd_off(qt, s)), st.vf[s], pacc);
+    const u32x4 x = lds_read16_at(qa + T::opnd_off(qt, s)), y = lds_read16_at(ga + T::opnd_off(qt, s));
+    if (s == 0) {
+      mfma32_v0<BF16>(sacc, x, st.kf[s]);
+      mfma32_v0<BF16>(pacc, y, st.vf[s]);
+    } else {
+      mfma32_v<BF16>(sacc, x, st.kf[s]);
+      mfma32_v<BF16>(pacc, y, st.vf[s]);
+    }
   }
+  mfma_vgpr_wait();
 }
 
 // Where a 32-query half lives: its tile's LSE*log2(e) and D in LDS (offset
@@ -438,15 +464,22 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
   f32x4 l4a = lds_f32x4(cur.lb + 4 * (qoff + 16)), d4a = lds_f32x4(cur.db + 4 * (qoff + 16));
   f32x4 l4b = lds_f32x4(cur.lb + 4 * (qoff + 24)), d4b = lds_f32x4(cur.db + 4 * (qoff + 24));
   __builtin_amdgcn_sched_barrier(0);
-  f32x16 ns = f32x16{}, np = f32x16{};
+  f32x16 ns, np;
   float zprev = 0.f, dsprev = 0.f;
 #pragma unroll
   for (int i = 0; i < kNP; ++i) {
     const int s = i >> 1;
-    if (i & 1)
-      np = mfma32<BF16>(ob[i], st.vf[s], np);
-    else
-      ns = mfma32<BF16>(ob[i], st.kf[s], ns);
+    if (i < 2) {
+      if (i & 1)
+        mfma32_v0<BF16>(np, ob[i], st.vf[s]);
+      else
+        mfma32_v0<BF16>(ns, ob[i], st.kf[s]);
+    } else {
+      if (i & 1)
+        mfma32_v<BF16>(np, ob[i], st.vf[s]);
+      else
+        mfma32_v<BF16>(ns, ob[i], st.kf[s]);
+    }
     if (i + kPF < kNP)
       ob[i + kPF] = opnd(nop, nxt.qt, i + kPF);
     else
@@ -488,6 +521,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
       st.dk[dt] = mfma32<BF16>(sf[mm], tb[j], st.dk[dt]);
     else
       st.dv[dt] = mfma32<BF16>(zf[mm], tb[j], st.dv[dt]);
+    if (j == 0) mfma_vgpr_wait();  // ns, np (read from j = kLag on) are complete
     if (j + kPF < kNA)
       tb[j + kPF] = tr_pair(j + kPF);
     else
