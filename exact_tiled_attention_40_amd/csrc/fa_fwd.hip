@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   using T = MTile<D, kBC>;
   constexpr int kNS = 2 * (D / 16);  // S^T products per tile (two 32-key tiles x D/16 k-steps)
   constexpr int kNO = 4 * (D / 32);  // O^T products per tile (four 16-key slices x D/32 tiles)
-  constexpr int kPF = 4;             // LDS operand reads in flight (products ahead)
+  constexpr int kPF = 3;             // LDS operand reads in flight (products ahead)
   constexpr int kLoads = 2 * (T::kBlocks / kWaves);  // 1 KB tile loads per wave per tile step
   static_assert(kLoads == 2 || kLoads == 4, "load spreading assumes 2 or 4 loads per step");
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
