@@ -56,8 +56,10 @@ def _load():
         lib.oracle_keep_mask.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.POINTER(ctypes.c_uint8)]
         lib.oracle_keep_mask.restype = None
+        u8p = ctypes.POINTER(ctypes.c_uint8)
         common = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
-                  ctypes.c_double, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int, ip]
+                  ctypes.c_double, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int, ip,
+                  u8p, ctypes.c_int, ctypes.c_int]
         lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp] + common
         lib.oracle_fwd.restype = None
         lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp] + common
@@ -117,43 +119,60 @@ def _prep(*xs):
     return [np.ascontiguousarray(x, dtype=np.float64) for x in xs]
 
 
+def _mask(block_mask, block: int, nseq: int, H: int, lens):
+    """(pointer, block, blocks per side) of an optional [nseq, H, nb, nb] block mask."""
+    if block_mask is None:
+        return None, 1, 0, None
+    m = np.ascontiguousarray(np.asarray(block_mask, dtype=np.uint8))
+    nb = -(-int(max(lens)) // block) if len(lens) else 0
+    assert m.ndim == 4 and m.shape[0] == nseq and m.shape[1] == H and m.shape[2] == m.shape[3], m.shape
+    assert m.shape[2] >= nb
+    return m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), int(block), int(m.shape[2]), m
+
+
 def forward(q, k, v, *, scale: float, causal: bool, N: int | None = None, lengths=None,
-            dropout_p: float = 0.0, seed: int = 0, heads=None):
+            dropout_p: float = 0.0, seed: int = 0, heads=None, block_mask=None, block: int = 128):
     """O and LSE of attention.  q, k, v: float64 [tokens, H, d].
 
     Fixed length: pass N (sequence length; tokens = B*N).  Varlen: pass the
     list of sequence lengths.  ``heads`` = optional list of (sequence, head)
     pairs to compute; other entries of O and LSE are returned as NaN.
-    Dropout keep bits depend on (seed, sequence index, head, row, col)."""
+    Dropout keep bits depend on (seed, sequence index, head, row, col).
+    ``block_mask`` = optional uint8 [sequences, H, nb, nb]: element (i, j) of
+    a head is visible only if entry (i // block, j // block) is nonzero; rows
+    with no visible key get O = 0 and LSE = -inf."""
     lib = _load()
     q, k, v = _prep(q, k, v)
     T, H, d = q.shape
     starts, lens = _seq_layout(T, N, lengths)
     nsel, sel = _sel(heads)
+    mptr, blk, nb, _keep = _mask(block_mask, block, len(lens), H, lens)
     o = np.full_like(q, np.nan)
     lse = np.full((T, H), np.nan, dtype=np.float64)
     lib.oracle_fwd(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse), len(lens), _iptr(starts),
                    _iptr(lens), H, d, float(scale), int(bool(causal)), float(np.float32(dropout_p)),
                    dropout_threshold(dropout_p) if dropout_p > 0 else 0, int(seed) & (2**64 - 1),
-                   nsel, _iptr(sel))
+                   nsel, _iptr(sel), mptr, blk, nb)
     return o, lse
 
 
 def backward(q, k, v, dout, *, scale: float, causal: bool, N: int | None = None, lengths=None,
-             dropout_p: float = 0.0, seed: int = 0, heads=None):
-    """dQ, dK, dV of L = sum(O * dout), with O = forward(q, k, v)."""
+             dropout_p: float = 0.0, seed: int = 0, heads=None, block_mask=None, block: int = 128):
+    """dQ, dK, dV of L = sum(O * dout), with O = forward(q, k, v) (same
+    optional block mask)."""
     lib = _load()
     q, k, v, dout = _prep(q, k, v, dout)
     T, H, d = q.shape
     starts, lens = _seq_layout(T, N, lengths)
     nsel, sel = _sel(heads)
+    mptr, blk, nb, _keep = _mask(block_mask, block, len(lens), H, lens)
     dq = np.full_like(q, np.nan)
     dk = np.full_like(q, np.nan)
     dv = np.full_like(q, np.nan)
     lib.oracle_bwd(_dptr(q), _dptr(k), _dptr(v), _dptr(dout), _dptr(dq), _dptr(dk), _dptr(dv),
                    len(lens), _iptr(starts), _iptr(lens), H, d, float(scale), int(bool(causal)),
                    float(np.float32(dropout_p)), dropout_threshold(dropout_p) if dropout_p > 0 else 0,
-                   int(seed) & (2**64 - 1), nsel, _iptr(sel))
+                   int(seed) & (2**64 - 1), nsel, _iptr(sel), mptr, blk, nb)
     return dq, dk, dv
 
 

@@ -22,6 +22,10 @@
  *   step 3  O[i]    = sum_j Z[i][j] v[j]
  *
  * "Visible" means j <= i for causal attention, every j < L otherwise.
+ * With a block mask (block-sparse attention, the block-sparse mode named in
+ * section 5.2 of the tiemojia.cn article), element (i, j) is visible only if
+ * in addition the mask entry of query block i / blk and key block j / blk is
+ * nonzero.  A row with no visible key has O = 0, LSE = -inf and no gradient.
  * The N x N matrices S, P (and dP in the backward) are materialised per
  * head on purpose: this is the standard algorithm the tiled method is
  * exactly equivalent to (lab write-up section 3.2).
@@ -110,9 +114,18 @@ typedef struct {
     uint32_t thresh;  /* floor(p * 2^32) */
     uint64_t seed;
     int b, h;         /* counter indices of this head */
+    const uint8_t* bmask; /* NULL, or [nbq][nbk] block mask of this head */
+    int blk, nbk;     /* block size (rows and columns), mask row length */
 } head_args;
 
+/* Columns 0 .. n_visible - 1 may be visible (causal prefix); visible() is
+ * the full test. */
 static int n_visible(const head_args* a, int i, int L) { return a->causal ? i + 1 : L; }
+static int visible(const head_args* a, int i, int j)
+{
+    if (a->causal && j > i) return 0;
+    return !a->bmask || a->bmask[(size_t)(i / a->blk) * a->nbk + j / a->blk] != 0;
+}
 
 static double dot(const double* x, const double* y, int d)
 {
@@ -130,13 +143,22 @@ static void softmax_rows(const double* q, const double* k, long ld, int L, int d
         double* row = P + (size_t)i * L;
         int nv = n_visible(a, i, L);
         double m = -INFINITY;
+        int any = 0;
         for (int j = 0; j < nv; ++j) {
+            if (!visible(a, i, j)) continue;
             row[j] = a->scale * dot(q + (size_t)i * ld, k + (size_t)j * ld, d);
             if (row[j] > m) m = row[j];
+            any = 1;
+        }
+        if (!any) {                 /* no visible key: P = 0, LSE = -inf */
+            for (int j = 0; j < L; ++j) row[j] = 0.0;
+            if (lse) lse[i] = -INFINITY;
+            continue;
         }
         double sum = 0.0;
-        for (int j = 0; j < nv; ++j) sum += exp(row[j] - m);
-        for (int j = 0; j < nv; ++j) row[j] = exp(row[j] - m) / sum;
+        for (int j = 0; j < nv; ++j)
+            if (visible(a, i, j)) sum += exp(row[j] - m);
+        for (int j = 0; j < nv; ++j) row[j] = visible(a, i, j) ? exp(row[j] - m) / sum : 0.0;
         for (int j = nv; j < L; ++j) row[j] = 0.0;
         if (lse) lse[i] = m + log(sum);
     }
@@ -154,10 +176,12 @@ static double keep_factor(const head_args* a, int i, int j)
  * apart (ld = H*d for a [tokens, H, d] tensor).  lse is indexed lse[i*lse_ld]. */
 void oracle_fwd_head(const double* q, const double* k, const double* v, long ld, int L, int d,
                      double scale, int causal, double dropout_p, uint32_t thresh, uint64_t seed,
-                     int b, int h, double* o, double* lse, long lse_ld)
+                     int b, int h, const uint8_t* bmask, int blk, int nbk,
+                     double* o, double* lse, long lse_ld)
 {
     if (L <= 0) return;
-    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h};
+    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h,
+                   bmask, blk, nbk};
     double* P = (double*)malloc(sizeof(double) * (size_t)L * L);
     double* l = (double*)malloc(sizeof(double) * (size_t)L);
     softmax_rows(q, k, ld, L, d, &a, P, l);
@@ -167,6 +191,7 @@ void oracle_fwd_head(const double* q, const double* k, const double* v, long ld,
         for (int c = 0; c < d; ++c) oi[c] = 0.0;
         int nv = n_visible(&a, i, L);
         for (int j = 0; j < nv; ++j) {
+            if (!visible(&a, i, j)) continue;
             double z = P[(size_t)i * L + j] * keep_factor(&a, i, j);
             const double* vj = v + (size_t)j * ld;
             for (int c = 0; c < d; ++c) oi[c] += z * vj[c];
@@ -184,7 +209,8 @@ void oracle_fwd_head_tiled(const double* q, const double* k, const double* v, lo
                            int b, int h, int Br, int Bc, double* o, double* lse, long lse_ld)
 {
     if (L <= 0) return;
-    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h};
+    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h,
+                   NULL, 1, 0};
     double* acc = (double*)malloc(sizeof(double) * (size_t)Br * d);
     double* m = (double*)malloc(sizeof(double) * (size_t)Br);
     double* l = (double*)malloc(sizeof(double) * (size_t)Br);
@@ -238,10 +264,12 @@ void oracle_fwd_head_tiled(const double* q, const double* k, const double* v, lo
 void oracle_bwd_head(const double* q, const double* k, const double* v, const double* dout,
                      long ld, int L, int d, double scale, int causal, double dropout_p,
                      uint32_t thresh, uint64_t seed, int b, int h,
+                     const uint8_t* bmask, int blk, int nbk,
                      double* dq, double* dk, double* dv)
 {
     if (L <= 0) return;
-    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h};
+    head_args a = {scale, causal, dropout_p > 0.0, 1.0 / (1.0 - dropout_p), thresh, seed, b, h,
+                   bmask, blk, nbk};
     size_t LL = (size_t)L * L;
     double* P = (double*)malloc(sizeof(double) * LL);
     double* dS = (double*)malloc(sizeof(double) * LL);
@@ -256,13 +284,14 @@ void oracle_bwd_head(const double* q, const double* k, const double* v, const do
         const double* pr = P + (size_t)i * L;
         double rowdot = 0.0;
         for (int j = 0; j < nv; ++j) {
+            if (!visible(&a, i, j)) { dsr[j] = 0.0; zr[j] = 0.0; continue; }
             double kf = keep_factor(&a, i, j);
             double dp = dot(dout + (size_t)i * ld, v + (size_t)j * ld, d) * kf;
             dsr[j] = dp;
             zr[j] = pr[j] * kf;
             rowdot += pr[j] * dp;
         }
-        for (int j = 0; j < nv; ++j) dsr[j] = pr[j] * (dsr[j] - rowdot);
+        for (int j = 0; j < nv; ++j) dsr[j] = pr[j] * (dsr[j] - rowdot);  /* 0 where invisible */
         for (int j = nv; j < L; ++j) { dsr[j] = 0.0; zr[j] = 0.0; }
     }
     /* dQ = scale dS K */
@@ -327,7 +356,14 @@ typedef struct {
     double scale, p;
     uint32_t thresh;
     uint64_t seed;
+    const uint8_t* bmask;   /* NULL, or [nseq][H][nb][nb] */
+    int blk, nb;
 } batch_ctx;
+
+static const uint8_t* head_mask(const batch_ctx* c, int s, int h)
+{
+    return c->bmask ? c->bmask + ((size_t)s * c->H + h) * (size_t)c->nb * c->nb : NULL;
+}
 
 static void fwd_one(int s, int h, void* vctx)
 {
@@ -335,7 +371,7 @@ static void fwd_one(int s, int h, void* vctx)
     long ld = (long)c->H * c->d;
     size_t off = (size_t)c->starts[s] * ld + (size_t)h * c->d;
     oracle_fwd_head(c->q + off, c->k + off, c->v + off, ld, c->lens[s], c->d, c->scale, c->causal,
-                    c->p, c->thresh, c->seed, s, h, c->o + off,
+                    c->p, c->thresh, c->seed, s, h, head_mask(c, s, h), c->blk, c->nb, c->o + off,
                     c->lse + (size_t)c->starts[s] * c->H + h, c->H);
 }
 
@@ -346,25 +382,29 @@ static void bwd_one(int s, int h, void* vctx)
     size_t off = (size_t)c->starts[s] * ld + (size_t)h * c->d;
     oracle_bwd_head(c->q + off, c->k + off, c->v + off, c->dout + off, ld, c->lens[s], c->d,
                     c->scale, c->causal, c->p, c->thresh, c->seed, s, h,
-                    c->dq + off, c->dk + off, c->dv + off);
+                    head_mask(c, s, h), c->blk, c->nb, c->dq + off, c->dk + off, c->dv + off);
 }
 
+/* bmask: NULL, or a [nseq][H][nb][nb] uint8 block mask with blocks of blk
+ * rows and columns (nb = ceil(max sequence length / blk)). */
 void oracle_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
                 int nseq, const int* starts, const int* lens, int H, int d, double scale, int causal,
-                double dropout_p, uint32_t thresh, uint64_t seed, int nsel, const int* sel)
+                double dropout_p, uint32_t thresh, uint64_t seed, int nsel, const int* sel,
+                const uint8_t* bmask, int blk, int nb)
 {
     batch_ctx c = {q, k, v, NULL, o, lse, NULL, NULL, NULL, starts, lens, H, d, causal,
-                   scale, dropout_p, thresh, seed};
+                   scale, dropout_p, thresh, seed, bmask, blk, nb};
     run_pairs(nseq, starts, lens, H, nsel, sel, fwd_one, &c);
 }
 
 void oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
                 double* dq, double* dk, double* dv,
                 int nseq, const int* starts, const int* lens, int H, int d, double scale, int causal,
-                double dropout_p, uint32_t thresh, uint64_t seed, int nsel, const int* sel)
+                double dropout_p, uint32_t thresh, uint64_t seed, int nsel, const int* sel,
+                const uint8_t* bmask, int blk, int nb)
 {
     batch_ctx c = {q, k, v, dout, NULL, NULL, dq, dk, dv, starts, lens, H, d, causal,
-                   scale, dropout_p, thresh, seed};
+                   scale, dropout_p, thresh, seed, bmask, blk, nb};
     run_pairs(nseq, starts, lens, H, nsel, sel, bwd_one, &c);
 }
 

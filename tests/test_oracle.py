@@ -368,3 +368,135 @@ def test_tiny_dropout_probability_equals_no_dropout():
     o1, _ = fwd(q, k, v, 0.5, True, dropout_p=1e-12, seed=3)
     o2, _ = fwd(q, k, v, 0.5, True)
     np.testing.assert_allclose(o1, o2, atol=1e-12)
+
+
+# ------------------------------------------------------------ block mask
+# Block-sparse attention (the block-sparse mode of the tiemojia.cn article,
+# section 5.2): element (i, j) is visible only where the block mask entry of
+# (i // block, j // block) is nonzero.
+
+def _element_mask(bm, N, block, causal):
+    """[B, H, N, N] boolean element mask (True = visible) from a block mask."""
+    idx = np.arange(N) // block
+    m = bm[:, :, idx][:, :, :, idx].astype(bool)
+    if causal:
+        m = m & np.tril(np.ones((N, N), dtype=bool))
+    return m
+
+
+def _random_block_mask(B, H, nb, seed, density=0.5):
+    bm = (np.random.default_rng(seed).random((B, H, nb, nb)) < density).astype(np.uint8)
+    for r in range(nb):
+        bm[:, :, r, r] = 1  # every row keeps its diagonal block: no empty row
+    return bm
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_matches_torch_sdpa_fp64(causal):
+    B, N, H, d, s, blk = 2, 45, 3, 16, 0.3, 8
+    nb = -(-N // blk)
+    q, k, v = rnd((B, N, H, d), 200), rnd((B, N, H, d), 201), rnd((B, N, H, d), 202)
+    bm = _random_block_mask(B, H, nb, 203)
+    o, lse = oracle.forward(q.reshape(-1, H, d), k.reshape(-1, H, d), v.reshape(-1, H, d), scale=s,
+                            causal=causal, N=N, block_mask=bm, block=blk)
+    em = torch.tensor(_element_mask(bm, N, blk, causal))
+    tq, tk, tv = (torch.tensor(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=em, scale=s)
+    np.testing.assert_allclose(o.reshape(B, N, H, d), ref.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    S = torch.einsum("bhnd,bhmd->bhnm", tq, tk) * s
+    ref_lse = torch.logsumexp(S.masked_fill(~em, float("-inf")), -1).permute(0, 2, 1).numpy()
+    np.testing.assert_allclose(lse.reshape(B, N, H), ref_lse, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_grads_match_torch_autograd_fp64(causal):
+    B, N, H, d, s, blk = 1, 37, 2, 8, 0.4, 6
+    nb = -(-N // blk)
+    q, k, v, do = (rnd((B, N, H, d), 210 + t) for t in range(4))
+    bm = _random_block_mask(B, H, nb, 215)
+    dq, dk, dv = oracle.backward(*(x.reshape(-1, H, d) for x in (q, k, v, do)), scale=s, causal=causal, N=N,
+                                 block_mask=bm, block=blk)
+    em = torch.tensor(_element_mask(bm, N, blk, causal))
+    tq, tk, tv = (torch.tensor(x).permute(0, 2, 1, 3).requires_grad_() for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=em, scale=s)
+    out.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    for mine, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine.reshape(B, N, H, d), t.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_all_ones_equals_dense(causal):
+    N, H, d, blk = 29, 2, 8, 8
+    q, k, v, do = (rnd((N, H, d), 220 + t) for t in range(4))
+    bm = np.ones((1, H, 4, 4), dtype=np.uint8)
+    o0, l0 = oracle.forward(q, k, v, scale=0.5, causal=causal, N=N)
+    o1, l1 = oracle.forward(q, k, v, scale=0.5, causal=causal, N=N, block_mask=bm, block=blk)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    g0 = oracle.backward(q, k, v, do, scale=0.5, causal=causal, N=N)
+    g1 = oracle.backward(q, k, v, do, scale=0.5, causal=causal, N=N, block_mask=bm, block=blk)
+    for a, b in zip(g0, g1):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_diagonal_mask_equals_separate_sequences(causal):
+    # a block-diagonal mask cuts one sequence into independent pieces of one
+    # block each, which is what the varlen layout computes
+    N, H, d, blk = 40, 2, 8, 8
+    nb = N // blk
+    q, k, v, do = (rnd((N, H, d), 230 + t) for t in range(4))
+    bm = np.zeros((1, H, nb, nb), dtype=np.uint8)
+    for r in range(nb):
+        bm[0, :, r, r] = 1
+    o1, l1 = oracle.forward(q, k, v, scale=0.7, causal=causal, N=N, block_mask=bm, block=blk)
+    o2, l2 = oracle.forward(q, k, v, scale=0.7, causal=causal, lengths=[blk] * nb)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+    g1 = oracle.backward(q, k, v, do, scale=0.7, causal=causal, N=N, block_mask=bm, block=blk)
+    g2 = oracle.backward(q, k, v, do, scale=0.7, causal=causal, lengths=[blk] * nb)
+    for a, b in zip(g1, g2):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+def test_block_mask_empty_rows_and_unseen_keys():
+    N, d, blk = 24, 8, 8
+    q, k, v, do = (rnd((N, d), 240 + t) for t in range(4))
+    bm = np.ones((1, 1, 3, 3), dtype=np.uint8)
+    bm[0, 0, 1, :] = 0      # queries 8..15 see nothing
+    bm[0, 0, :, 2] = 0      # keys 16..23 are seen by no query
+    o, lse = fwd(q, k, v, 0.5, False, block_mask=bm, block=blk)
+    assert np.all(o[8:16] == 0.0) and np.all(np.isneginf(lse[8:16]))
+    assert np.all(np.isfinite(lse[:8])) and np.all(np.isfinite(lse[16:]))
+    dq, dk, dv = bwd(q, k, v, do, 0.5, False, block_mask=bm, block=blk)
+    assert np.all(dq[8:16] == 0.0)
+    assert np.all(dk[16:] == 0.0) and np.all(dv[16:] == 0.0)
+    # the remaining rows see exactly keys 0..15: plain attention over them
+    S = q @ k[:16].T * 0.5
+    P = np.exp(S - S.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    np.testing.assert_allclose(o[:8], (P @ v[:16])[:8], atol=1e-12)
+    np.testing.assert_allclose(o[16:], (P @ v[:16])[16:], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_backward_finite_differences(causal):
+    L, d, s, blk = 12, 4, 0.6, 4
+    q, k, v, do = (rnd((L, d), 250 + t) for t in range(4))
+    bm = np.array([[[[1, 0, 1], [0, 0, 0], [1, 1, 0]]]], dtype=np.uint8)  # row block 1 empty
+    kw = dict(block_mask=bm, block=blk)
+    dq, dk, dv = bwd(q, k, v, do, s, causal, **kw)
+
+    def loss(qq, kk, vv):
+        o, _ = fwd(qq, kk, vv, s, causal, **kw)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for trial in range(3):
+            delta = rnd((L, d), 260 + 10 * which + trial)
+            args = [q, k, v]
+            plus = [a + h * delta if t == which else a for t, a in enumerate(args)]
+            minus = [a - h * delta if t == which else a for t, a in enumerate(args)]
+            fd = (loss(*plus) - loss(*minus)) / (2 * h)
+            an = float((grad * delta).sum())
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
