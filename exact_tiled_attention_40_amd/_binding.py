@@ -19,6 +19,8 @@ _LIB_PATH = os.path.join(_PKG, "libfa.so")
 
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
+FA_MASK_BLOCK = 128       # rows and columns of one block-mask entry
+FA_MASK_MAX_N = 65536     # longest sequence the block-sparse calls accept
 _DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 
 
@@ -46,6 +48,10 @@ def _load():
     lib.fa_backward_stage.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
     lib.fa_backward_workspace_size.restype = ctypes.c_size_t
+    lib.fa_forward_block_sparse.argtypes = lib.fa_forward.argtypes + [vp]
+    lib.fa_forward_block_sparse.restype = i
+    lib.fa_backward_block_sparse.argtypes = lib.fa_backward.argtypes + [vp]
+    lib.fa_backward_block_sparse.restype = i
     lib.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
     lib.fa_dropout_mask.restype = i
     lib.fa_strerror.argtypes = [i]
@@ -104,10 +110,21 @@ def _same_geometry(ref, *ts):
             raise ValueError("q, k, v (and dq, dk, dv) must share shape, strides, dtype and device")
 
 
+def _block_mask(block_mask, B, H, N, device):
+    nb = -(-N // FA_MASK_BLOCK)
+    if block_mask.dtype != torch.uint8 or block_mask.device != device or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous uint8 tensor on q's device")
+    if tuple(block_mask.shape) != (B, H, nb, nb):
+        raise ValueError(f"block_mask must be [B, H, nb, nb] = {(B, H, nb, nb)}")
+    return _ptr(block_mask)
+
+
 def fa_forward(q, k, v, *, scale=None, causal=False, cu_seqlens=None, max_seqlen=None, dropout_p=0.0, seed=0,
-               out=None, lse=None, stream=None):
+               out=None, lse=None, stream=None, block_mask=None):
     """Returns (o, lse).  o is contiguous with q's logical shape; lse is float32
-    [B, N, H] (fixed length) or [total, H] (varlen)."""
+    [B, N, H] (fixed length) or [total, H] (varlen).  With ``block_mask``
+    (uint8 [B, H, nb, nb], nb = ceil(N / FA_MASK_BLOCK)) this calls
+    fa_forward_block_sparse."""
     _same_geometry(q, k, v)
     if q.dtype not in _DTYPES:
         raise FAError(3, fa_strerror(3))
@@ -118,9 +135,12 @@ def fa_forward(q, k, v, *, scale=None, causal=False, cu_seqlens=None, max_seqlen
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
-    _check(_lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
-                           int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
-                           _stream(stream), _DTYPES[q.dtype], ld))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+            _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1), _stream(stream), _DTYPES[q.dtype], ld)
+    if block_mask is None:
+        _check(_lib.fa_forward(*args))
+    else:
+        _check(_lib.fa_forward_block_sparse(*args, _block_mask(block_mask, B, H, N, q.device)))
     return out, lse
 
 
@@ -129,13 +149,14 @@ def fa_backward_workspace_size(B: int, N: int, H: int, d: int) -> int:
 
 
 def fa_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=None, max_seqlen=None,
-                dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+                dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None, stream=None, block_mask=None):
     """Returns (dq, dk, dv).  Freshly allocated gradients are contiguous; pass
     dq/dk/dv views (e.g. into a packed [B, N, 3, H, d] buffer) with q's
-    strides to write in place."""
+    strides to write in place.  With ``block_mask`` this calls
+    fa_backward_block_sparse (same mask as the forward)."""
     return _backward(None, q, k, v, o, lse, dout, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
                      max_seqlen=max_seqlen, dropout_p=dropout_p, seed=seed, dq=dq, dk=dk, dv=dv,
-                     workspace=workspace, stream=stream)
+                     workspace=workspace, stream=stream, block_mask=block_mask)
 
 
 def fa_backward_stage(stage, q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=None,
@@ -151,7 +172,7 @@ def fa_backward_stage(stage, q, k, v, o, lse, dout, *, scale=None, causal=False,
 
 
 def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_seqlen, dropout_p, seed, dq, dk,
-              dv, workspace, stream):
+              dv, workspace, stream, block_mask=None):
     _same_geometry(q, k, v)
     if q.dtype not in _DTYPES:
         raise FAError(3, fa_strerror(3))
@@ -171,7 +192,11 @@ def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_se
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
             float(scale), int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
             _stream(stream), _DTYPES[q.dtype], ld, _ptr(workspace), workspace.numel() * workspace.element_size())
-    if stage is None:
+    if block_mask is not None:
+        if stage is not None:
+            raise ValueError("block-sparse backward runs as one call")
+        _check(_lib.fa_backward_block_sparse(*args, _block_mask(block_mask, B, H, N, q.device)))
+    elif stage is None:
         _check(_lib.fa_backward(*args))
     else:
         _check(_lib.fa_backward_stage(stage, *args))

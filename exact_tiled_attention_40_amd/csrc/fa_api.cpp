@@ -41,6 +41,17 @@ int check_common(int B, int H, int N, int d, float scale, float dropout_p, int d
   s->drop_thresh = s->dropout ? (uint32_t)t : 0u;
   s->drop_rescale = s->dropout ? 1.0f / (1.0f - dropout_p) : 1.0f;
   s->seed = seed;
+  s->bmask = nullptr;
+  s->nb = 0;
+  return FA_OK;
+}
+
+// Block-sparse additions to a checked launch description.
+int check_block_mask(const uint8_t* block_mask, int N, fa::AttnShape* s) {
+  if (!block_mask) return FA_ERR_NULL_POINTER;
+  if (N > FA_MASK_MAX_N) return FA_ERR_UNSUPPORTED;
+  s->bmask = block_mask;
+  s->nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   return FA_OK;
 }
 
@@ -48,17 +59,32 @@ int check_common(int B, int H, int N, int d, float scale, float dropout_p, int d
 
 extern "C" {
 
-int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-               float scale, int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
-               int dtype, int64_t ld_qkv) {
+static int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                        int d, float scale, int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                        void* stream, int dtype, int64_t ld_qkv, const uint8_t* block_mask, bool sparse) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
   fa::AttnShape s;
-  const int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
+  int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
   if (rc != FA_OK) return rc;
+  if (sparse && (rc = check_block_mask(block_mask, N, &s)) != FA_OK) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGNMENT;
   const hipError_t e = fa::launch_forward(s, q, k, v, o, lse, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+               int dtype, int64_t ld_qkv) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, dropout_p, seed, stream, dtype,
+                      ld_qkv, nullptr, false);
+}
+
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int N, int d, float scale, int causal, const int32_t* cu_seqlens, float dropout_p,
+                            uint64_t seed, void* stream, int dtype, int64_t ld_qkv, const uint8_t* block_mask) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, dropout_p, seed, stream, dtype,
+                      ld_qkv, block_mask, true);
 }
 
 size_t fa_backward_workspace_size(int B, int N, int H, int d) {
@@ -73,11 +99,13 @@ size_t fa_backward_workspace_size(int B, int N, int H, int d) {
 static int backward_impl(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                          int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
-                         int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes) {
+                         int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes,
+                         const uint8_t* block_mask, bool sparse) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
   fa::AttnShape s;
-  const int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
+  int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
   if (rc != FA_OK) return rc;
+  if (sparse && (rc = check_block_mask(block_mask, N, &s)) != FA_OK) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_ALIGNMENT;
@@ -97,7 +125,16 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream, int dtype, int64_t ld_qkv,
                 void* workspace, size_t workspace_bytes) {
   return backward_impl(fa::kBwdAll, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
-                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes);
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, nullptr, false);
+}
+
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                             float scale, int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                             void* stream, int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes,
+                             const uint8_t* block_mask) {
+  return backward_impl(fa::kBwdAll, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, block_mask, true);
 }
 
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -106,7 +143,7 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes) {
   if (stage < 0 || stage > 1) return FA_ERR_BAD_ARGUMENT;
   return backward_impl(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
-                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes);
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, nullptr, false);
 }
 
 int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed, void* stream) {

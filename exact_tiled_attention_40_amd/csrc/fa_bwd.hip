@@ -73,6 +73,8 @@ struct BwdArgs {
   uint32_t drop_thresh;
   float drop_rescale;
   uint32_t seed_lo, seed_hi;
+  const uint8_t* bmask;  // block-sparse instantiations only: [B, H, nb, nb]
+  int nb;
 };
 
 __device__ __forceinline__ void seq_range(const BwdArgs& a, int b, int& start, int& L) {
@@ -94,7 +96,7 @@ __device__ __forceinline__ float keep_factor(const BwdArgs& a, int b, int h, int
 }
 
 // ---------------------------------------------------------------- dQ (+ D)
-template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
 __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   using T = MTile<D, kBC>;
   constexpr int kNS = 2 * (D / 16);  // S^T and dP^T products per 32-key half (D/16 k-steps each)
@@ -102,6 +104,10 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int kPF = 2;             // LDS operand reads in flight (products ahead)
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
+  // block-sparse: the key tiles the workgroup visits, in order
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ uint8_t tflag[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int tcount[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,8 +175,11 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
       asm volatile("" : "+v"(gf[s]));
     }
   }
-  // queries past the end: Q = dO = 0 and LSE = 0 give P = 1, dP = 0, dS = 0
-  const float lse2 = qi < L ? a.lse[(int64_t)(start + qi) * a.H + h] * kLog2e : 0.f;
+  // queries past the end: Q = dO = 0 and LSE = 0 give P = 1, dP = 0, dS = 0.
+  // A query that sees no key (block-sparse) has LSE = -inf; +inf in its place
+  // makes every P of the row 0 wherever it is recomputed.
+  float lse2 = qi < L ? a.lse[(int64_t)(start + qi) * a.H + h] * kLog2e : 0.f;
+  if constexpr (SPARSE) lse2 = lse2 == -INFINITY ? INFINITY : lse2;
   if (qi < L && h2 == 0) {
     a.delta[(int64_t)(start + qi) * a.H + h] = delta;
     a.lse2[(int64_t)(start + qi) * a.H + h] = lse2;
@@ -196,7 +205,25 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   const uint32_t ob0 = T::opnd_base(lane, 0), ob1 = T::opnd_base(lane, 1);
   const uint32_t tb0 = T::tr_base(lane, 0), tb1 = T::tr_base(lane, 1);
 
-  issue_tile(0, 0);
+  // Visited key tiles: all tiles 0 .. ntiles-1, or (block-sparse) the listed
+  // ones.  Buffers follow the position k in that sequence; tile_at(k) is the
+  // tile index.
+  int n_list = ntiles;
+  if constexpr (SPARSE) {
+    if (w == 0) {
+      const uint8_t* mrow = a.bmask + (((int64_t)b * a.H + h) * a.nb + q0 / kMaskBlock) * a.nb;
+      const int n = build_tile_list(mrow, nullptr, 0, 1, ntiles, tlist, tflag, lane);
+      if (lane == 0) tcount[0] = n;
+    }
+    __syncthreads();
+    n_list = __builtin_amdgcn_readfirstlane(tcount[0]);
+  }
+  auto tile_at = [&](int k) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(tlist[k]);
+    else return k;
+  };
+
+  if (n_list > 0) issue_tile(tile_at(0) * kBC, 0);
   wait_vmem();
   __syncthreads();
 
@@ -205,9 +232,9 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   // interleaved, their K/V operands read kPF products ahead; the first K^T
   // transpose reads; P and dS; dQ^T += K^T dS^T with its K^T operands read
   // kPF products ahead.
-  auto tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+  auto tile = [&](int k, int t, auto mask_tag) __attribute__((always_inline)) {  // position k, tile t
     constexpr bool kMask = decltype(mask_tag)::value;
-    const int cur = t & 1;
+    const int cur = k & 1;
     const int j0 = t * kBC;
     uint32_t k0 = ks0 + cur * T::kBytes + ob0, k1 = ks0 + cur * T::kBytes + ob1;
     uint32_t v0 = vs0 + cur * T::kBytes + ob0, v1 = vs0 + cur * T::kBytes + ob1;
@@ -288,18 +315,23 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   // mask code, and the loop keeps one accumulator path.  Every wave still
   // issues its share of every tile load and joins every barrier.
   const int last = qw >= L ? -1 : (CAUSAL ? min(ntiles - 1, (qw + 31) / kBC) : ntiles - 1);
-  int t = 0;
-  for (; t < last; ++t) {
-    if (t + 1 < ntiles) issue_tile((t + 1) * kBC, (t & 1) ^ 1);
-    tile(t, std::false_type{});
+  int k = 0;
+  int tk = n_list > 0 ? tile_at(0) : -1;
+  for (; k < n_list && tk < last; ++k) {
+    const int tk1 = k + 1 < n_list ? tile_at(k + 1) : -1;
+    if (tk1 >= 0) issue_tile(tk1 * kBC, (k & 1) ^ 1);
+    tile(k, tk, std::false_type{});
     wait_vmem();
     __syncthreads();
+    tk = tk1;
   }
-  for (; t < ntiles; ++t) {
-    if (t + 1 < ntiles) issue_tile((t + 1) * kBC, (t & 1) ^ 1);
-    if (t == last) tile(t, std::true_type{});
+  for (; k < n_list; ++k) {
+    const int tk1 = k + 1 < n_list ? tile_at(k + 1) : -1;
+    if (tk1 >= 0) issue_tile(tk1 * kBC, (k & 1) ^ 1);
+    if (tk == last) tile(k, tk, std::true_type{});
     wait_vmem();
     __syncthreads();
+    tk = tk1;
   }
 
   // ---- epilogue: register r of tile dt holds head-dim element
@@ -549,7 +581,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
   pacc = np;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   using T = MTile<D, kBR>;
   constexpr int kNB = 3;  // Q/dO/LSE/D tile buffers
@@ -558,6 +590,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float ls[kNB][kBR];
   __shared__ __attribute__((aligned(16))) float dls[kNB][kBR];
   __shared__ __attribute__((aligned(16))) float spare[64];
+  // block-sparse: the query tiles the workgroup visits, in order
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ uint8_t tflag[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int tcount[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -647,8 +683,27 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t ob0 = T::opnd_base(lane, 0), ob1 = T::opnd_base(lane, 1);
   const uint32_t tb0 = T::tr_base(lane, 0), tb1 = T::tr_base(lane, 1);
 
-  if (ntiles > 0) issue_tile(i_begin, 0);
-  if (ntiles > 1) issue_tile(i_begin + kBR, 1);
+  // Visited query tiles: all tiles 0 .. ntiles-1 (from i_begin), or
+  // (block-sparse) the listed ones.  Buffers follow the position k in that
+  // sequence; tile_at(k) is the tile index.
+  int n_list = ntiles;
+  if constexpr (SPARSE) {
+    if (w == 0) {
+      const uint8_t* mcol = a.bmask + ((int64_t)b * a.H + h) * a.nb * a.nb + j0 / kMaskBlock;
+      const int n = build_tile_list(mcol, nullptr, i_begin / kBR, a.nb, ntiles, tlist, tflag, lane);
+      if (lane == 0) tcount[0] = n;
+    }
+    __syncthreads();
+    n_list = __builtin_amdgcn_readfirstlane(tcount[0]);
+  }
+  auto tile_at = [&](int k) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(tlist[k]);
+    else return k;
+  };
+  const int t_first = n_list > 0 ? tile_at(0) : 0;
+
+  if (n_list > 0) issue_tile(i_begin + t_first * kBR, 0);
+  if (n_list > 1) issue_tile(i_begin + tile_at(1) * kBR, 1);
   wait_vmem();
   __syncthreads();
 
@@ -666,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     pf[i] = lds_read16_at(base + T::opnd_off(1, s));
   }
   {
-    const HalfCtx c0{ls0 + 16 * h2, dls0 + 16 * h2, i_begin, 0};
+    const HalfCtx c0{ls0 + 16 * h2, dls0 + 16 * h2, i_begin + t_first * kBR, 0};
     float zprev = 0.f, dsprev = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -683,11 +738,13 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  auto iteration = [&](int t, auto mask) {
+  // Iteration at position t of the visited tiles (tiles tk, tk1, tk2 at
+  // positions t, t+1, t+2; -1 past the end).
+  auto iteration = [&](int t, int tk, int tk1, int tk2, auto mask) {
     constexpr bool kMask = decltype(mask)::value;
     const int buf = t % kNB;
     const int nbuf = (t + 1) % kNB;
-    const int i0 = i_begin + t * kBR;
+    const int i0 = i_begin + tk * kBR;
     // tile t + 1 has landed; every wave is done with tile t - 1's buffers
     // (the reads still in flight here touch tiles t and t + 1 only)
     wait_vmem();
@@ -697,8 +754,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     // half's look-ahead products: Q and dO blocks at even products, LSE or D
     // (waves 0 and 1) at product 1.  Past the last tile the buffer ranges
     // are empty: the loads fetch nothing and fill the free buffer with zeros.
-    const int i2 = i0 + 2 * kBR;
-    const int rows = t + 2 < ntiles ? min(kBR, L - i2) : 0;
+    const int i2 = i_begin + max(tk2, 0) * kBR;
+    const int rows = tk2 >= 0 ? min(kBR, L - i2) : 0;
     const __amdgpu_buffer_rsrc_t qr =
         make_rsrc(qbase + (int64_t)min(i2, L - 1) * ld, rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u);
     const __amdgpu_buffer_rsrc_t gr =
@@ -731,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     uint32_t lb = ls0 + buf * kBR * 4 + 16 * h2, db = dls0 + buf * kBR * 4 + 16 * h2;
     uint32_t nlb = ls0 + nbuf * kBR * 4 + 16 * h2, ndb = dls0 + nbuf * kBR * 4 + 16 * h2;
     asm volatile("" : "+v"(lb), "+v"(db), "+v"(nlb), "+v"(ndb));
-    const HalfCtx h0{lb, db, i0, 0}, h1{lb, db, i0, 1}, n0{nlb, ndb, i0 + kBR, 0};
+    const HalfCtx h0{lb, db, i0, 0}, h1{lb, db, i0, 1}, n0{nlb, ndb, i_begin + max(tk1, 0) * kBR, 0};
     // On the last tile the look-ahead work reads a stale buffer and is
     // discarded; doing it anyway keeps the tile one basic block.  Masked
     // tiles come first, so the look-ahead into the next tile may use this
@@ -744,9 +801,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   // Causal: only the first two tiles (queries j0 .. j0+127) hold queries
   // before some key of the block, so only they are masked.
   int t = 0;
+  int tk = n_list > 0 ? t_first : -1;
+  int tk1 = n_list > 1 ? tile_at(1) : -1;
   if (CAUSAL)
-    for (; t < min(ntiles, 2); ++t) iteration(t, std::true_type{});
-  for (; t < ntiles; ++t) iteration(t, std::false_type{});
+    for (; t < n_list && tk < 2; ++t) {
+      const int tk2 = t + 2 < n_list ? tile_at(t + 2) : -1;
+      iteration(t, tk, tk1, tk2, std::true_type{});
+      tk = tk1;
+      tk1 = tk2;
+    }
+  for (; t < n_list; ++t) {
+    const int tk2 = t + 2 < n_list ? tile_at(t + 2) : -1;
+    iteration(t, tk, tk1, tk2, std::false_type{});
+    tk = tk1;
+    tk1 = tk2;
+  }
 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
@@ -787,21 +856,27 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
-hipError_t launch_bwd_t(const AttnShape& s, const BwdArgs& args, int stages, hipStream_t stream) {
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
+hipError_t launch_bwd_s(const AttnShape& s, const BwdArgs& args, int stages, hipStream_t stream) {
   if (stages & kBwdDq) {
     const int64_t nb = (int64_t)args.nqb * s.B * s.H;
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT>), dim3((unsigned)nb), dim3(kThreadsQ), 0, stream,
-                       args);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb), dim3(kThreadsQ),
+                       0, stream, args);
   }
   if (stages & kBwdKV) {
     const int64_t nb = (int64_t)args.nkb * s.B * s.H;
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, DROPOUT>), dim3((unsigned)nb), dim3(kThreads), 0,
-                       stream, args);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb), dim3(kThreads),
+                       0, stream, args);
   }
   return hipGetLastError();
+}
+
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+hipError_t launch_bwd_t(const AttnShape& s, const BwdArgs& args, int stages, hipStream_t stream) {
+  return args.bmask ? launch_bwd_s<D, BF16, CAUSAL, DROPOUT, true>(s, args, stages, stream)
+                    : launch_bwd_s<D, BF16, CAUSAL, DROPOUT, false>(s, args, stages, stream);
 }
 
 template <int D, bool BF16>
@@ -843,6 +918,8 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
   a.drop_rescale = s.drop_rescale;
   a.seed_lo = (uint32_t)s.seed;
   a.seed_hi = (uint32_t)(s.seed >> 32);
+  a.bmask = s.bmask;
+  a.nb = s.nb;
   if (s.d == 64)
     return s.bf16 ? launch_bwd_d<64, true>(s, a, stages, stream) : launch_bwd_d<64, false>(s, a, stages, stream);
   return s.bf16 ? launch_bwd_d<128, true>(s, a, stages, stream) : launch_bwd_d<128, false>(s, a, stages, stream);

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -185,15 +187,38 @@ __device__ __forceinline__ void buffer_load_lds4_addr(__amdgpu_buffer_rsrc_t r, 
       : "memory");
 }
 
-// Direct HBM -> LDS loads through the compiler builtin (it sets M0 itself):
-// every lane's 16 (or 4) bytes land at lds + 16*lane (4*lane).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voffset,
-                                           0, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 4, voffset,
-                                           0, 0, 0);
+// ------------------------------------------------------- block-sparse lists
+// Block masks have square blocks of kMaskBlock rows (queries) by kMaskBlock
+// columns (keys); the kernels' 64-row tiles are halves of mask blocks.
+constexpr int kMaskBlock = 128;
+constexpr int kMaxSparseTiles = 1024;  // 64-row tiles per sequence (N <= 65536)
+static_assert(kMaskBlock == FA_MASK_BLOCK && kMaxSparseTiles * 64 == FA_MASK_MAX_N,
+              "block-mask geometry must match the C ABI");
+
+// Compacted list of the tiles one workgroup visits under a block mask, built
+// by a single wave.  Tile t (0 <= t < ntiles) reads mask byte
+// ((t0 + t) / 2) * stride of row m0 and, if m1 is not null, of row m1; it is
+// listed when either byte is nonzero, with flag bit 0 / bit 1 set for a
+// nonzero byte of m0 / m1.  Returns the number of listed tiles (uniform).
+__device__ __forceinline__ int build_tile_list(const uint8_t* m0, const uint8_t* m1, int t0, int64_t stride,
+                                               int ntiles, uint16_t* list, uint8_t* flags, int lane) {
+  int n = 0;
+  for (int base = 0; base < ntiles; base += 64) {
+    const int t = base + lane;
+    int f = 0;
+    if (t < ntiles) {
+      const int64_t off = (int64_t)((t0 + t) >> 1) * stride;
+      f = (m0[off] != 0 ? 1 : 0) | (m1 != nullptr && m1[off] != 0 ? 2 : 0);
+    }
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(f != 0);
+    const int pos = n + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (f != 0) {
+      list[pos] = (uint16_t)t;
+      flags[pos] = (uint8_t)f;
+    }
+    n += __builtin_popcountll(bal);
+  }
+  return n;
 }
 
 // A tile of ROWS rows (a multiple of 32) of D 16-bit elements in LDS, laid

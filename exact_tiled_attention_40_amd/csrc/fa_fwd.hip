@@ -56,9 +56,11 @@ struct FwdArgs {
   uint32_t drop_thresh;
   float drop_rescale;
   uint32_t seed_lo, seed_hi;
+  const uint8_t* bmask;  // block-sparse instantiations only: [B, H, nb, nb]
+  int nb;
 };
 
-template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   using T = MTile<D, kBC>;
   constexpr int kNS = 2 * (D / 16);  // S^T products per tile (two 32-key tiles x D/16 k-steps)
@@ -68,6 +70,11 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   static_assert(kLoads == 2 || kLoads == 4, "load spreading assumes 2 or 4 loads per step");
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
+  // block-sparse: the key tiles the workgroup visits (in order) and which of
+  // its two 128-query mask rows each one serves
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ uint8_t tflag[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int tcount[SPARSE ? 1 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   // Vector phase of tile t: mask, online softmax of sacc (register r of key
   // half kt holds key t*kBC + kt*32 + 8*(r/4) + 4*h2 + r%4), dropout, and the
   // P^T operands of the next matrix phase.
-  auto v_phase = [&](int t, bool may_mask, auto&& hook) __attribute__((always_inline)) {
+  auto v_phase = [&](int t, bool may_mask, bool skip, auto&& hook) __attribute__((always_inline)) {
     // hook(u) for each of the kLoads tile loads, spread over four points
     auto at = [&](int point) {
       if constexpr (kLoads == 4) hook(point);
@@ -264,6 +271,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
     mx = halves_max(mx) * a.scale_log2;
+    // block-sparse: a tile listed for the other mask row only contributes
+    // nothing (no max update, every probability 0)
+    if constexpr (SPARSE) mx = skip ? -INFINITY : mx;
     at(1);
     const bool grow = mx > m_run + kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -276,7 +286,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float m_use = m_run == -INFINITY ? 0.f : m_run;
+    if constexpr (SPARSE) m_use = skip ? INFINITY : m_use;
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -323,64 +334,104 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   // tiles are double-buffered (K(t), V(t) in buffer t % 2): K(t+2) and V(t+1)
   // are issued at the start of slot 2t + 1 (their buffers were last read in
   // slot 2t) and waited for at the end of slot 2t + 2.
-  issue(kbase, ks0, 0);
-  issue(vbase, vs0, 0);
-  if (ntiles > 1) issue(kbase, ks0 + T::kBytes, kBC);
+  // Visited key tiles: all tiles 0 .. ntiles-1, or (block-sparse) the listed
+  // ones.  Buffers follow the position k in that sequence; tile_at(k) is the
+  // tile index.
+  int n_list = ntiles;
+  if constexpr (SPARSE) {
+    if (w == 0) {
+      const uint8_t* mrow = a.bmask + ((int64_t)b * a.H + h) * a.nb * a.nb;
+      const int r0 = q0 / kMaskBlock;
+      const int n = build_tile_list(mrow + (int64_t)r0 * a.nb, r0 + 1 < a.nb ? mrow + (int64_t)(r0 + 1) * a.nb : nullptr,
+                                    0, 1, ntiles, tlist, tflag, lane);
+      if (lane == 0) tcount[0] = n;
+    }
+    __syncthreads();
+    n_list = __builtin_amdgcn_readfirstlane(tcount[0]);
+  }
+  auto tile_at = [&](int k) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(tlist[k]);
+    else return k;
+  };
+  const int grp = w / (kWaves / 2);  // also the wave's 128-query mask row in the workgroup
+  auto skip_at = [&](int k) __attribute__((always_inline)) -> bool {
+    if constexpr (SPARSE) return ((__builtin_amdgcn_readfirstlane(tflag[k]) >> grp) & 1) == 0;
+    else return false;
+  };
+
+  if (n_list > 0) {
+    issue(kbase, ks0, tile_at(0) * kBC);
+    issue(vbase, vs0, tile_at(0) * kBC);
+  }
+  if (n_list > 1) issue(kbase, ks0 + T::kBytes, tile_at(1) * kBC);
   wait_vmem();
   __syncthreads();
-  const int grp = w / (kWaves / 2);
-  // Load u (0 <= u < kLoads) of this wave's share of slot 2t + 1: blocks of
-  // K(t+2) into buffer t % 2, then of V(t+1) into buffer (t+1) % 2 (both
-  // buffers were last read in slot 2t).
-  auto load_part = [&](int t, int u) __attribute__((always_inline)) {
+  // Load u (0 <= u < kLoads) of this wave's share of slot 2k + 1: blocks of
+  // the K tile at position k+2 into buffer k % 2, then of the V tile at
+  // position k+1 into buffer (k+1) % 2 (both buffers were last read in slot
+  // 2k).  tk1, tk2 = tile indices at positions k+1, k+2 (or -1).
+  auto load_part = [&](int k, int tk1, int tk2, int u) __attribute__((always_inline)) {
     constexpr int per = T::kBlocks / kWaves;
     const bool isk = u < per;
-    const int tt = isk ? t + 2 : t + 1;
-    if (tt >= ntiles) return;
+    const int tt = isk ? tk2 : tk1;
+    if (tt < 0) return;
     const int j0 = tt * kBC;
     const uint32_t bytes = (uint32_t)(min(kBC, L - j0) - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t r = make_rsrc((isk ? kbase : vbase) + (int64_t)j0 * ld, bytes);
-    const uint32_t lds = isk ? ks0 + (t & 1) * T::kBytes : vs0 + ((t + 1) & 1) * T::kBytes;
+    const uint32_t lds = isk ? ks0 + (k & 1) * T::kBytes : vs0 + ((k + 1) & 1) * T::kBytes;
     T::load(r, lds, row_bytes, (isk ? u : u - per) * kWaves + w, lane);
   };
+  auto tile_or_none = [&](int k) __attribute__((always_inline)) { return k < n_list ? tile_at(k) : -1; };
   auto no_hook = [](int) {};
   // The loop for one group G, whose wave-level schedule is fixed at compile
-  // time: group 0 spreads its loads of slot 2t + 1 between the products of
-  // M(t), group 1 through the softmax of V(t), so that no wave stalls on a
+  // time: group 0 spreads its loads of slot 2k + 1 between the products of
+  // M(k), group 1 through the softmax of V(k), so that no wave stalls on a
   // burst of load issues.
   auto run = [&](auto G) __attribute__((always_inline)) {
     constexpr int g = decltype(G)::value;
-    if (last >= 0) s_products(0);
+    // the wave computes the visited tiles up to its last one: a prefix
+    if (n_list > 0 && tile_at(0) <= last) s_products(0);
     if (g == 1) __syncthreads();  // slot 0: group 1 idle
-    // Only the wave's last tile can hold masked keys (causal diagonal or the
-    // ragged end), so the tiles before it run without mask code.
-    int t = 0;
-    for (; t < last; ++t) {
-      auto loads = [&](int u) { load_part(t, u); };
-      if constexpr (g == 1) v_phase(t, false, loads);
-      else v_phase(t, false, no_hook);
-      if (g == 0 && t > 0) wait_vmem();
+    // Only the wave's last computed tile can hold masked keys (causal
+    // diagonal or the ragged end), so the tiles before it run without mask
+    // code.
+    int k = 0;
+    int tk = n_list > 0 ? tile_at(0) : -1;
+    int tk1 = tile_or_none(1);
+    for (; tk1 >= 0 && tk1 <= last; ++k) {
+      const int tk2 = tile_or_none(k + 2);
+      const bool skip = skip_at(k);
+      auto loads = [&](int u) { load_part(k, tk1, tk2, u); };
+      if constexpr (g == 1) v_phase(tk, false, skip, loads);
+      else v_phase(tk, false, skip, no_hook);
+      if (g == 0 && k > 0) wait_vmem();
       __syncthreads();
-      if constexpr (g == 0) m_phase(t, true, loads);
-      else m_phase(t, true, no_hook);
+      if constexpr (g == 0) m_phase(k, true, loads);
+      else m_phase(k, true, no_hook);
       if (g == 1) wait_vmem();
       __syncthreads();
+      tk = tk1;
+      tk1 = tk2;
     }
-    // The wave's last tile, then the slots of tiles it does not need (it
-    // still issues its share of their loads).
-    for (; t < ntiles; ++t) {
+    // The wave's last computed tile, then the slots of tiles it does not
+    // need (it still issues its share of their loads).
+    for (; k < n_list; ++k) {
+      const int tk2 = tile_or_none(k + 2);
+      const bool mine = tk <= last;
       if (g == 1)
-        for (int u = 0; u < kLoads; ++u) load_part(t, u);
-      if (t == last) v_phase(t, true, no_hook);
-      if (g == 0 && t > 0) wait_vmem();
+        for (int u = 0; u < kLoads; ++u) load_part(k, tk1, tk2, u);
+      if (mine) v_phase(tk, true, skip_at(k), no_hook);
+      if (g == 0 && k > 0) wait_vmem();
       __syncthreads();
       if (g == 0)
-        for (int u = 0; u < kLoads; ++u) load_part(t, u);
-      if (t == last) m_phase(t, false, no_hook);
+        for (int u = 0; u < kLoads; ++u) load_part(k, tk1, tk2, u);
+      if (mine) m_phase(k, false, no_hook);
       if (g == 1) wait_vmem();
       __syncthreads();
+      tk = tk1;
+      tk1 = tk2;
     }
-    if (g == 0) __syncthreads();  // slot 2 * ntiles: group 0 idle
+    if (g == 0) __syncthreads();  // slot 2 * n_list: group 0 idle
   };
   if (grp == 0)
     run(std::integral_constant<int, 0>{});
@@ -407,8 +458,12 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
 hipError_t launch_fwd_t(const FwdArgs& args, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT>), dim3(nblocks), dim3(kThreads), 0, stream,
-                     args);
+  if (args.bmask)
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, true>), dim3(nblocks), dim3(kThreads), 0,
+                       stream, args);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, false>), dim3(nblocks), dim3(kThreads), 0,
+                       stream, args);
   return hipGetLastError();
 }
 
@@ -457,6 +512,8 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
   a.drop_rescale = s.drop_rescale;
   a.seed_lo = (uint32_t)s.seed;
   a.seed_hi = (uint32_t)(s.seed >> 32);
+  a.bmask = s.bmask;
+  a.nb = s.nb;
   const int64_t nblocks = (int64_t)a.nqb * s.B * s.H;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (s.d == 64)

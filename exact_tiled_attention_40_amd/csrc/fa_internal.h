@@ -18,6 +18,8 @@ struct AttnShape {
   uint32_t drop_thresh;    // floor(p * 2^32)
   float drop_rescale;      // 1 / (1 - p)
   uint64_t seed;
+  const uint8_t* bmask;    // block mask [B, H, nb, nb] (device) or nullptr: dense
+  int nb;                  // mask blocks per side, ceil(N / 128)
 };
 
 hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, const void* v, void* o,

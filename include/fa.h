@@ -128,6 +128,38 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
                       int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes);
 
+/* ---------------------------------------------------------- block-sparse
+ * Block-sparse attention: the block-sparse mode the tiemojia.cn article
+ * names in section 5.2 (with masks converted to block format, its section
+ * 2.3).  A block mask switches whole FA_MASK_BLOCK x FA_MASK_BLOCK blocks of
+ * the score matrix on or off; the kernels skip the tiles of blocks that are
+ * off, so work and time scale with the number of blocks that are on.
+ *   block_mask : DEVICE uint8 [B, H, nb, nb], nb = ceil(N / FA_MASK_BLOCK),
+ *                owned by the caller.  Entry (b, h, r, c) nonzero lets the
+ *                queries r*FA_MASK_BLOCK .. +FA_MASK_BLOCK-1 of sequence b,
+ *                head h see the keys c*FA_MASK_BLOCK .. +FA_MASK_BLOCK-1
+ *                (positions local to the sequence for varlen).  With
+ *                causal, j <= i applies as well.
+ *   A query that sees no key gets O = 0 and lse = -inf, and contributes no
+ *   gradient.  N must be <= FA_MASK_MAX_N (FA_ERR_UNSUPPORTED otherwise);
+ *   a NULL block_mask returns FA_ERR_NULL_POINTER.  Every other argument,
+ *   layout and error is as for fa_forward / fa_backward, which the calls
+ *   below equal when every mask entry is nonzero. */
+#define FA_MASK_BLOCK 128
+#define FA_MASK_MAX_N 65536
+
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int N, int d, float scale, int causal,
+                            const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                            int dtype, int64_t ld_qkv, const uint8_t* block_mask);
+
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             int B, int H, int N, int d, float scale, int causal,
+                             const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                             void* stream, int dtype, int64_t ld_qkv, void* workspace,
+                             size_t workspace_bytes, const uint8_t* block_mask);
+
 /* Dropout keep mask of a single (b, h) head as the fused kernels draw it:
  * keep[i * N + j] = 1 if element (i, j) is kept, 0 if dropped, for
  * 0 <= i, j < N (both local indices; causal masking is NOT applied).  keep

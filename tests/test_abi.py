@@ -25,8 +25,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_backward", "fa_backward_stage", "fa_backward_workspace_size",
-                                    "fa_dropout_mask", "fa_forward", "fa_strerror"]
+    assert declared_functions() == ["fa_backward", "fa_backward_block_sparse", "fa_backward_stage",
+                                    "fa_backward_workspace_size", "fa_dropout_mask", "fa_forward",
+                                    "fa_forward_block_sparse", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -50,6 +51,8 @@ def lib():
     L.fa_backward_workspace_size.argtypes = [i, i, i, i]
     L.fa_backward_workspace_size.restype = ctypes.c_size_t
     L.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
+    L.fa_forward_block_sparse.argtypes = L.fa_forward.argtypes + [vp]
+    L.fa_backward_block_sparse.argtypes = L.fa_backward.argtypes + [vp]
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     return L
@@ -131,3 +134,33 @@ def test_binding_fails_loudly_without_library(tmp_path):
     code = "import exact_tiled_attention_40_amd"
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "libfa.so is missing" in r.stderr
+
+
+# ------------------------------------------------------------ block-sparse
+
+def fwd_bs(lib, mask=P, **over):
+    a = dict(FWD_OK, **over)
+    return lib.fa_forward_block_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                       a["scale"], a["causal"], a["cu"], a["p"], a["seed"], a["stream"],
+                                       a["dtype"], a["ld"], mask)
+
+
+def test_block_sparse_forward_rejects_bad_arguments(lib):
+    assert fwd_bs(lib, mask=None) == 1                    # no mask
+    assert fwd_bs(lib, N=65537) == 3                      # longer than FA_MASK_MAX_N
+    assert fwd_bs(lib, q=None) == 1                       # the dense checks still apply
+    assert fwd_bs(lib, d=96) == 3
+    assert fwd_bs(lib, scale=float("nan")) == 4
+    assert fwd_bs(lib, o=P + 2) == 5
+
+
+def test_block_sparse_backward_rejects_bad_arguments(lib):
+    need = lib.fa_backward_workspace_size(1, 128, 2, 64)
+
+    def call(mask=P, N=128, ws=P, wsb=need):
+        return lib.fa_backward_block_sparse(P, P, P, P, P, P, P, P, P, 1, 2, N, 64, 0.125, 0, None, 0.0, 0,
+                                            None, 1, 0, ws, wsb, mask)
+    assert call(mask=None) == 1
+    assert call(N=70000, wsb=lib.fa_backward_workspace_size(1, 70000, 2, 64)) == 3
+    assert call(ws=None) == 6
+    assert call(wsb=need - 1) == 6

@@ -144,3 +144,19 @@ def as_f64_tokens(x: torch.Tensor):
     if x.dim() == 4:
         x = x.reshape(x.shape[0] * x.shape[1], x.shape[2], x.shape[3])
     return x.to(torch.float64).contiguous().numpy()
+
+
+def block_mask(B: int, H: int, N: int, density: float, seed: int, *, block: int = 128,
+               keep_diagonal: bool = True) -> torch.Tensor:
+    """Random uint8 block mask [B, H, nb, nb] (nb = ceil(N / block)) for
+    block-sparse attention: each entry is 1 with probability ``density``
+    (a seeded CPU torch.Generator draws one uniform per entry, row-major);
+    with ``keep_diagonal`` the diagonal blocks are forced to 1, so that no
+    query row is left without keys."""
+    nb = -(-N // block)
+    g = torch.Generator().manual_seed(seed)
+    m = (torch.rand(B, H, nb, nb, generator=g) < density).to(torch.uint8)
+    if keep_diagonal:
+        idx = torch.arange(nb)
+        m[:, :, idx, idx] = 1
+    return m
