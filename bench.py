@@ -2,6 +2,7 @@
 """Attention forward + backward throughput on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--block-density P]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 fa_forward (fused tiled forward) followed by the two backward kernels
@@ -15,7 +16,10 @@ prints one JSON line.
 
 Work convention: a visible (query, key) pair costs 4*d flops forward and
 10*d flops backward (B*H*N(N+1)/2 pairs causal, B*H*N^2 otherwise); masked
-work inside diagonal tiles is not counted.  Peak = MI355X dense bf16/fp16
+work inside diagonal tiles is not counted.  With --block-density P the
+block-sparse calls run under a random 128x128 block mask (each block on with
+probability P, diagonal blocks on) and only the pairs it leaves visible
+count.  Peak = MI355X dense bf16/fp16
 MFMA, 2.5 PFLOP/s.
 """
 from __future__ import annotations
@@ -48,6 +52,19 @@ def visible_pairs(wl, lengths=None) -> int:
     if wl.causal:
         return wl.H * sum(L * (L + 1) // 2 for L in lens)
     return wl.H * sum(L * L for L in lens)
+
+
+def visible_pairs_masked(wl, bm) -> int:
+    """Visible pairs under a [B, H, nb, nb] block mask (blocks of 128), with
+    the causal rule j <= i where the workload is causal."""
+    import numpy as np
+    blk, N = 128, wl.N
+    nb = bm.shape[-1]
+    sizes = np.minimum(blk, N - blk * np.arange(nb))            # rows (= columns) of each block
+    full = np.outer(sizes, sizes)                                 # pairs of a block with no causal cut
+    if wl.causal:
+        full = np.tril(full, -1) + np.diag(sizes * (sizes + 1) // 2)
+    return int((bm.astype(np.int64) * full[None, None]).sum())
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -166,6 +183,9 @@ def main() -> int:
     ap.add_argument("--copy-bytes", type=int, default=0, help="run only the counter calibration pass over this many bytes")
     ap.add_argument("--pmc-summary", default="", help="directory of rocprofv3 --pmc runs to turn into the traffic file")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30, help="bytes of the calibration pass of --pmc-summary")
+    ap.add_argument("--block-density", type=float, default=0.0,
+                    help="time the block-sparse calls with a random 128x128 block mask of this density "
+                         "(diagonal blocks kept); 0 = dense")
     ap.add_argument("--settle-s", type=float, default=1.5,
                     help="repeat the warm-up steps until this many seconds have passed (clock settling)")
     args = ap.parse_args()
@@ -203,6 +223,10 @@ def main() -> int:
     ws = torch.empty(fa.fa_backward_workspace_size(wl.B, wl.N, wl.H, wl.d), dtype=torch.uint8, device=dev)
     kw = dict(scale=wl.scale, causal=wl.causal, dropout_p=wl.dropout_p, seed=wl.seed)
     stream = torch.cuda.current_stream()
+    bm = None
+    if args.block_density > 0:
+        bm = workloads.block_mask(wl.B, wl.H, wl.N, args.block_density, seed=wl.seed + 1000)
+        kw["block_mask"] = bm.to(dev)
 
     def step(ev=None):
         if ev: ev[0].record(stream)
@@ -233,7 +257,7 @@ def main() -> int:
     ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
     step_ms = events[0][0].elapsed_time(events[-1][3]) / args.steps
 
-    pairs = visible_pairs(wl)
+    pairs = visible_pairs(wl) if bm is None else visible_pairs_masked(wl, bm.numpy())
     fwd_flops = 4.0 * wl.d * pairs
     bwd_flops = 10.0 * wl.d * pairs
     total_tflops = (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
@@ -270,8 +294,11 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
-                   "dropout_p": wl.dropout_p, "packed_qkv": wl.packed},
+        "config": {"workload": wl.name + (f"_blocksparse{args.block_density:g}" if bm is not None else ""),
+                   "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
+                   "dropout_p": wl.dropout_p, "packed_qkv": wl.packed,
+                   **({"block_density": args.block_density, "mask_blocks_on": int(bm.sum()),
+                       "mask_blocks": int(bm.numel()), "visible_pairs": pairs} if bm is not None else {})},
         "frac_of_peak": total_tflops / PEAK_TFLOPS,
         "fwd": {"tflops": fwd_tflops, "ms": ms["fa_fwd_kernel"], "frac": fwd_tflops / PEAK_TFLOPS},
         "bwd": {"tflops": bwd_tflops, "ms": bwd_ms, "frac": bwd_tflops / PEAK_TFLOPS},
@@ -280,7 +307,9 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if bm is not None:
+        line["roofline"]["traffic"] = None  # the traffic file covers the dense kernels
+    if not args.no_cpu_baseline and bm is None:
         line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_heads)
     print(json.dumps(line), flush=True)
     return 0

@@ -52,6 +52,8 @@ def _load():
     lib.fa_forward_block_sparse.restype = i
     lib.fa_backward_block_sparse.argtypes = lib.fa_backward.argtypes + [vp]
     lib.fa_backward_block_sparse.restype = i
+    lib.fa_backward_block_sparse_stage.argtypes = [i] + lib.fa_backward_block_sparse.argtypes
+    lib.fa_backward_block_sparse_stage.restype = i
     lib.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
     lib.fa_dropout_mask.restype = i
     lib.fa_strerror.argtypes = [i]
@@ -161,14 +163,15 @@ def fa_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=N
 
 def fa_backward_stage(stage, q, k, v, o, lse, dout, *, scale=None, causal=False, cu_seqlens=None,
                       max_seqlen=None, dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None,
-                      stream=None):
+                      stream=None, block_mask=None):
     """One backward stage (0: D and dQ, 1: dK and dV); the caller passes the
-    same dq/dk/dv and workspace to both, stage 0 first."""
+    same dq/dk/dv and workspace to both, stage 0 first.  With ``block_mask``
+    this calls fa_backward_block_sparse_stage."""
     if dq is None or dk is None or dv is None or workspace is None:
         raise ValueError("fa_backward_stage needs explicit dq, dk, dv and workspace")
     return _backward(int(stage), q, k, v, o, lse, dout, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
                      max_seqlen=max_seqlen, dropout_p=dropout_p, seed=seed, dq=dq, dk=dk, dv=dv,
-                     workspace=workspace, stream=stream)
+                     workspace=workspace, stream=stream, block_mask=block_mask)
 
 
 def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_seqlen, dropout_p, seed, dq, dk,
@@ -193,9 +196,11 @@ def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_se
             float(scale), int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
             _stream(stream), _DTYPES[q.dtype], ld, _ptr(workspace), workspace.numel() * workspace.element_size())
     if block_mask is not None:
-        if stage is not None:
-            raise ValueError("block-sparse backward runs as one call")
-        _check(_lib.fa_backward_block_sparse(*args, _block_mask(block_mask, B, H, N, q.device)))
+        m = _block_mask(block_mask, B, H, N, q.device)
+        if stage is None:
+            _check(_lib.fa_backward_block_sparse(*args, m))
+        else:
+            _check(_lib.fa_backward_block_sparse_stage(stage, *args, m))
     elif stage is None:
         _check(_lib.fa_backward(*args))
     else:

@@ -146,6 +146,16 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                        dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, nullptr, false);
 }
 
+int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
+                                   int N, int d, float scale, int causal, const int32_t* cu_seqlens,
+                                   float dropout_p, uint64_t seed, void* stream, int dtype, int64_t ld_qkv,
+                                   void* workspace, size_t workspace_bytes, const uint8_t* block_mask) {
+  if (stage < 0 || stage > 1) return FA_ERR_BAD_ARGUMENT;
+  return backward_impl(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, block_mask, true);
+}
+
 int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed, void* stream) {
   if (!keep) return FA_ERR_NULL_POINTER;
   if (b < 0 || h < 0 || N < 1 || (int64_t)N * N > ((int64_t)1 << 40)) return FA_ERR_BAD_SHAPE;

@@ -160,6 +160,16 @@ int fa_backward_block_sparse(const void* q, const void* k, const void* v, const 
                              void* stream, int dtype, int64_t ld_qkv, void* workspace,
                              size_t workspace_bytes, const uint8_t* block_mask);
 
+/* One of the two kernels fa_backward_block_sparse enqueues (stage 0: D and
+ * dQ, stage 1: dK and dV), as fa_backward_stage is for fa_backward. */
+int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, const void* v,
+                                   const void* o, const float* lse, const void* dout, void* dq,
+                                   void* dk, void* dv, int B, int H, int N, int d, float scale,
+                                   int causal, const int32_t* cu_seqlens, float dropout_p,
+                                   uint64_t seed, void* stream, int dtype, int64_t ld_qkv,
+                                   void* workspace, size_t workspace_bytes,
+                                   const uint8_t* block_mask);
+
 /* Dropout keep mask of a single (b, h) head as the fused kernels draw it:
  * keep[i * N + j] = 1 if element (i, j) is kept, 0 if dropped, for
  * 0 <= i, j < N (both local indices; causal masking is NOT applied).  keep

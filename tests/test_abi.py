@@ -25,7 +25,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_backward", "fa_backward_block_sparse", "fa_backward_stage",
+    assert declared_functions() == ["fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage",
+                                    "fa_backward_stage",
                                     "fa_backward_workspace_size", "fa_dropout_mask", "fa_forward",
                                     "fa_forward_block_sparse", "fa_strerror"]
 
@@ -53,6 +54,7 @@ def lib():
     L.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
     L.fa_forward_block_sparse.argtypes = L.fa_forward.argtypes + [vp]
     L.fa_backward_block_sparse.argtypes = L.fa_backward.argtypes + [vp]
+    L.fa_backward_block_sparse_stage.argtypes = [i] + L.fa_backward_block_sparse.argtypes
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     return L
@@ -164,3 +166,7 @@ def test_block_sparse_backward_rejects_bad_arguments(lib):
     assert call(N=70000, wsb=lib.fa_backward_workspace_size(1, 70000, 2, 64)) == 3
     assert call(ws=None) == 6
     assert call(wsb=need - 1) == 6
+    stage_args = (P, P, P, P, P, P, P, P, P, 1, 2, 128, 64, 0.125, 0, None, 0.0, 0, None, 1, 0, P, need)
+    assert lib.fa_backward_block_sparse_stage(2, *stage_args, P) == 4
+    assert lib.fa_backward_block_sparse_stage(-1, *stage_args, P) == 4
+    assert lib.fa_backward_block_sparse_stage(0, *stage_args, None) == 1
