@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
+    static_assert(T::kBlocks % kWavesQ == 0, "tile blocks must split evenly over the waves");
 #pragma unroll
     for (int u = 0; u < T::kBlocks / kWavesQ; ++u) {
       T::load(kr, ks0 + buf * T::kBytes, row_bytes, u * kWavesQ + w, lane);
@@ -469,7 +470,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
                                           Hook&& hook) {
   using T = MTile<D, kBR>;
   constexpr int kNP = D / 8;  // look-ahead products (S and dP, D/16 k-steps each)
-  constexpr int kPF = 4;      // LDS operand reads in flight (products ahead)
+  constexpr int kPF = D >= 64 ? 4 : 2;  // LDS operand reads in flight (products ahead)
   static_assert(kNP >= 2 * kPF, "prefetch window exceeds a phase");
   auto opnd = [&](const TileAddr& t, int qt, int i) {
     const int s = i >> 1;
@@ -666,6 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const int rows = min(kBR, L - i0);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qbase + (int64_t)i0 * ld, (uint32_t)(rows - 1) * row_bytes + D * 2);
     const __amdgpu_buffer_rsrc_t gr = make_rsrc(gbase + (int64_t)i0 * hd, (uint32_t)(rows - 1) * grow_bytes + D * 2);
+    static_assert(T::kBlocks % kWaves == 0, "tile blocks must split evenly over the waves");
 #pragma unroll
     for (int u = 0; u < T::kBlocks / kWaves; ++u) {
       T::load(qr, qs0 + buf * T::kBytes, row_bytes, u * kWaves + w, lane);
@@ -920,9 +922,13 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
   a.seed_hi = (uint32_t)(s.seed >> 32);
   a.bmask = s.bmask;
   a.nb = s.nb;
-  if (s.d == 64)
-    return s.bf16 ? launch_bwd_d<64, true>(s, a, stages, stream) : launch_bwd_d<64, false>(s, a, stages, stream);
-  return s.bf16 ? launch_bwd_d<128, true>(s, a, stages, stream) : launch_bwd_d<128, false>(s, a, stages, stream);
+  switch (s.d) {
+    case 32: return s.bf16 ? launch_bwd_d<32, true>(s, a, stages, stream) : launch_bwd_d<32, false>(s, a, stages, stream);
+    case 64: return s.bf16 ? launch_bwd_d<64, true>(s, a, stages, stream) : launch_bwd_d<64, false>(s, a, stages, stream);
+    case 96: return s.bf16 ? launch_bwd_d<96, true>(s, a, stages, stream) : launch_bwd_d<96, false>(s, a, stages, stream);
+    default: return s.bf16 ? launch_bwd_d<128, true>(s, a, stages, stream)
+                           : launch_bwd_d<128, false>(s, a, stages, stream);
+  }
 }
 
 }  // namespace fa

@@ -66,7 +66,11 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   constexpr int kNS = 2 * (D / 16);  // S^T products per tile (two 32-key tiles x D/16 k-steps)
   constexpr int kNO = 4 * (D / 32);  // O^T products per tile (four 16-key slices x D/32 tiles)
   constexpr int kPF = 3;             // LDS operand reads in flight (products ahead)
-  constexpr int kLoads = 2 * (T::kBlocks / kWaves);  // 1 KB tile loads per wave per tile step
+  // 1 KB blocks of a K or V tile per wave (wave w loads blocks w, w + kWaves,
+  // ...; with fewer blocks than a multiple of kWaves the last round is
+  // partial), and tile loads per wave per tile step
+  constexpr int kPer = (T::kBlocks + kWaves - 1) / kWaves;
+  constexpr int kLoads = 2 * kPer;
   static_assert(kLoads == 2 || kLoads == 4, "load spreading assumes 2 or 4 loads per step");
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
@@ -140,7 +144,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
     const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)j0 * ld, bytes);
 #pragma unroll
-    for (int u = 0; u < T::kBlocks / kWaves; ++u) T::load(r, lds, row_bytes, u * kWaves + w, lane);
+    for (int u = 0; u < kPer; ++u)
+      if (u * kWaves + w < T::kBlocks) T::load(r, lds, row_bytes, u * kWaves + w, lane);
   };
 
   f32x16 oacc[D / 32];
@@ -371,15 +376,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   // position k+1 into buffer (k+1) % 2 (both buffers were last read in slot
   // 2k).  tk1, tk2 = tile indices at positions k+1, k+2 (or -1).
   auto load_part = [&](int k, int tk1, int tk2, int u) __attribute__((always_inline)) {
-    constexpr int per = T::kBlocks / kWaves;
+    constexpr int per = kPer;
     const bool isk = u < per;
+    const int blk = (isk ? u : u - per) * kWaves + w;
+    if (blk >= T::kBlocks) return;
     const int tt = isk ? tk2 : tk1;
     if (tt < 0) return;
     const int j0 = tt * kBC;
     const uint32_t bytes = (uint32_t)(min(kBC, L - j0) - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t r = make_rsrc((isk ? kbase : vbase) + (int64_t)j0 * ld, bytes);
     const uint32_t lds = isk ? ks0 + (k & 1) * T::kBytes : vs0 + ((k + 1) & 1) * T::kBytes;
-    T::load(r, lds, row_bytes, (isk ? u : u - per) * kWaves + w, lane);
+    T::load(r, lds, row_bytes, blk, lane);
   };
   auto tile_or_none = [&](int k) __attribute__((always_inline)) { return k < n_list ? tile_at(k) : -1; };
   auto no_hook = [](int) {};
@@ -516,11 +523,16 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
   a.nb = s.nb;
   const int64_t nblocks = (int64_t)a.nqb * s.B * s.H;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (s.d == 64)
-    return s.bf16 ? launch_fwd_d<64, true>(s, a, (int)nblocks, stream)
-                  : launch_fwd_d<64, false>(s, a, (int)nblocks, stream);
-  return s.bf16 ? launch_fwd_d<128, true>(s, a, (int)nblocks, stream)
-                : launch_fwd_d<128, false>(s, a, (int)nblocks, stream);
+  switch (s.d) {
+    case 32: return s.bf16 ? launch_fwd_d<32, true>(s, a, (int)nblocks, stream)
+                           : launch_fwd_d<32, false>(s, a, (int)nblocks, stream);
+    case 64: return s.bf16 ? launch_fwd_d<64, true>(s, a, (int)nblocks, stream)
+                           : launch_fwd_d<64, false>(s, a, (int)nblocks, stream);
+    case 96: return s.bf16 ? launch_fwd_d<96, true>(s, a, (int)nblocks, stream)
+                           : launch_fwd_d<96, false>(s, a, (int)nblocks, stream);
+    default: return s.bf16 ? launch_fwd_d<128, true>(s, a, (int)nblocks, stream)
+                           : launch_fwd_d<128, false>(s, a, (int)nblocks, stream);
+  }
 }
 
 hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,

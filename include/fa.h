@@ -47,7 +47,10 @@
  *     (Salmon et al., SC'11).  Forward and backward must get the same seed and
  *     dropout_p.  dropout_p == 0 runs the no-dropout kernels.
  *   - dtype is FA_DTYPE_F16 or FA_DTYPE_BF16 for every tensor except lse and
- *     the workspace (float32).  d must be 64 or 128.
+ *     the workspace (float32).  d must be 32, 64, 96 or 128: head sizes up to
+ *     128 are the fused-kernel range in the tiemojia.cn article's list of
+ *     when the fused kernel applies (its engineering-considerations part);
+ *     the lab write-up, section 5.3, warns that kernels degrade past 192.
  *   - Pointers must be 16-byte aligned and ld_qkv a multiple of 8.
  *   - Outputs must not alias inputs; dq, dk and dv may point into one packed
  *     [B, N, 3, H, d] buffer when ld_qkv = 3*H*d.
@@ -71,7 +74,8 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
     FA_ERR_BAD_SHAPE = 2,      /* B, H or N < 1, or a size overflows */
-    FA_ERR_UNSUPPORTED = 3,    /* d not in {64, 128} or unknown dtype */
+    FA_ERR_UNSUPPORTED = 3,    /* d not in {32, 64, 96, 128}, unknown dtype,
+                                  or a block-sparse N above FA_MASK_MAX_N */
     FA_ERR_BAD_ARGUMENT = 4,   /* scale not finite, dropout_p not in [0, 1) */
     FA_ERR_ALIGNMENT = 5,      /* pointer not 16-byte aligned or bad ld_qkv */
     FA_ERR_WORKSPACE = 6,      /* workspace NULL or smaller than required */
@@ -129,9 +133,9 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes);
 
 /* ---------------------------------------------------------- block-sparse
- * Block-sparse attention: the block-sparse mode the tiemojia.cn article
- * names in section 5.2 (with masks converted to block format, its section
- * 2.3).  A block mask switches whole FA_MASK_BLOCK x FA_MASK_BLOCK blocks of
+ * Block-sparse attention: the block-sparse mode the coreui.cn
+ * FlashAttention-2 how-to names in section 5.2 (with masks converted to
+ * block format, its section 2.3).  A block mask switches whole FA_MASK_BLOCK x FA_MASK_BLOCK blocks of
  * the score matrix on or off; the kernels skip the tiles of blocks that are
  * off, so work and time scale with the number of blocks that are on.
  *   block_mask : DEVICE uint8 [B, H, nb, nb], nb = ceil(N / FA_MASK_BLOCK),

@@ -23,7 +23,8 @@
  *
  * "Visible" means j <= i for causal attention, every j < L otherwise.
  * With a block mask (block-sparse attention, the block-sparse mode named in
- * section 5.2 of the tiemojia.cn article), element (i, j) is visible only if
+ * section 5.2 of the coreui.cn FlashAttention-2 how-to), element (i, j) is
+ * visible only if
  * in addition the mask entry of query block i / blk and key block j / blk is
  * nonzero.  A row with no visible key has O = 0, LSE = -inf and no gradient.
  * The N x N matrices S, P (and dP in the backward) are materialised per

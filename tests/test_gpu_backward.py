@@ -51,6 +51,13 @@ SMALL = [
     (1, 4, 384, 64, "bf16", True),
     (3, 1, 191, 128, "f16", False),
     (1, 2, 1000, 128, "bf16", True),
+    # the smaller and in-between head sizes
+    (1, 2, 1, 32, "bf16", True),
+    (2, 2, 333, 32, "f16", False),
+    (1, 3, 517, 32, "bf16", True),
+    (1, 1, 1, 96, "f16", False),
+    (2, 2, 300, 96, "bf16", True),
+    (1, 2, 700, 96, "f16", False),
 ]
 
 
@@ -73,7 +80,7 @@ def test_backward_varlen_dropout():
     check(workloads.custom(0, 2, 0, 128, "bf16", True, lengths=[5, 130, 77], dropout_p=0.3, seed=19))
 
 
-@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+@pytest.mark.parametrize("d,causal", [(64, False), (128, True), (32, True), (96, False)])
 def test_backward_fixed_dropout(d, causal):
     check(workloads.custom(2, 2, 150, d, "f16", causal, dropout_p=0.2, seed=21))
 

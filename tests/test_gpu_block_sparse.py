@@ -81,6 +81,8 @@ CASES = [
     (1, 1, 1000, 128, "bf16", True, 0.3),
     (1, 3, 384, 64, "bf16", False, 0.0),
     (2, 1, 1111, 128, "f16", False, 0.7),
+    (1, 2, 600, 32, "bf16", True, 0.5),
+    (1, 2, 500, 96, "f16", False, 0.4),
 ]
 
 

@@ -45,6 +45,13 @@ SMALL = [
     (1, 4, 384, 64, "bf16", True),
     (3, 1, 191, 128, "f16", False),
     (1, 2, 1000, 128, "bf16", True),
+    # the smaller and in-between head sizes
+    (1, 2, 1, 32, "bf16", True),
+    (2, 2, 333, 32, "f16", False),
+    (1, 3, 517, 32, "bf16", True),
+    (1, 1, 1, 96, "f16", False),
+    (2, 2, 300, 96, "bf16", True),
+    (1, 2, 700, 96, "f16", False),
 ]
 
 

@@ -371,8 +371,8 @@ def test_tiny_dropout_probability_equals_no_dropout():
 
 
 # ------------------------------------------------------------ block mask
-# Block-sparse attention (the block-sparse mode of the tiemojia.cn article,
-# section 5.2): element (i, j) is visible only where the block mask entry of
+# Block-sparse attention (the block-sparse mode of the coreui.cn
+# FlashAttention-2 how-to, section 5.2): element (i, j) is visible only where the block mask entry of
 # (i // block, j // block) is nonzero.
 
 def _element_mask(bm, N, block, causal):
