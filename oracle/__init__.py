@@ -70,6 +70,9 @@ def _load():
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp,
                                               ctypes.c_long]
         lib.oracle_fwd_head_tiled.restype = None
+        lib.oracle_decode.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ip, ctypes.c_double, ctypes.c_int]
+        lib.oracle_decode.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -188,6 +191,24 @@ def forward_tiled_head(q, k, v, *, scale: float, causal: bool, Br: int, Bc: int,
                               float(np.float32(dropout_p)),
                               dropout_threshold(dropout_p) if dropout_p > 0 else 0,
                               int(seed) & (2**64 - 1), b, h, Br, Bc, _dptr(o), _dptr(lse), 1)
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, *, scale: float, causal: bool, seqlens_k=None):
+    """KV-cache decode step: q [B, nq, H, d] against the first seqlens_k[b]
+    tokens of k_cache, v_cache [B, nk_max, H, d] (all nk_max if None); the nq
+    queries are the last nq positions of their sequence (causal: query t sees
+    keys j <= L - nq + t).  Returns O [B, nq, H, d] and LSE [B, nq, H]."""
+    lib = _load()
+    q, k, v = _prep(q, k_cache, v_cache)
+    B, nq, H, d = q.shape
+    nk = k.shape[1]
+    assert k.shape == (B, nk, H, d) and v.shape == k.shape
+    lk = None if seqlens_k is None else np.ascontiguousarray(np.asarray(seqlens_k, dtype=np.int32))
+    o = np.zeros_like(q)
+    lse = np.zeros((B, nq, H), dtype=np.float64)
+    lib.oracle_decode(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse), B, H, nq, nk, d, _iptr(lk),
+                      float(scale), int(bool(causal)))
     return o, lse
 
 

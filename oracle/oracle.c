@@ -409,6 +409,49 @@ void oracle_bwd(const double* q, const double* k, const double* v, const double*
     run_pairs(nseq, starts, lens, H, nsel, sel, bwd_one, &c);
 }
 
+/* ------------------------------------------------------------ KV-cache decode */
+
+/* Decode step of inference with a KV cache (the cache use described in
+ * section 6.1 of the lab write-up): nq new query tokens attend to the lk
+ * cached keys and values of their sequence, the new tokens being the last nq
+ * positions of it, so that with causal masking query t (0 <= t < nq) sees
+ * keys j <= lk - nq + t (bottom-right alignment).  Steps 1-3 as above on the
+ * nq x lk score matrix.  q, o: [B, nq, H, d]; k, v: [B, nk_max, H, d] of
+ * which the first lk[b] tokens are valid; lse: [B, nq, H].  A query that
+ * sees no key gets O = 0, LSE = -inf. */
+void oracle_decode(const double* q, const double* k, const double* v, double* o, double* lse,
+                   int B, int H, int nq, int nk_max, int d, const int* lk, double scale, int causal)
+{
+    #pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            int L = lk ? lk[b] : nk_max;
+            double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+            for (int t = 0; t < nq; ++t) {
+                const double* qt = q + (((size_t)b * nq + t) * H + h) * d;
+                double* ot = o + (((size_t)b * nq + t) * H + h) * d;
+                int nv = causal ? L - nq + t + 1 : L;
+                if (nv > L) nv = L;
+                for (int c = 0; c < d; ++c) ot[c] = 0.0;
+                if (nv <= 0) { lse[((size_t)b * nq + t) * H + h] = -INFINITY; continue; }
+                double m = -INFINITY;
+                for (int j = 0; j < nv; ++j) {
+                    s[j] = scale * dot(qt, k + (((size_t)b * nk_max + j) * H + h) * d, d);
+                    if (s[j] > m) m = s[j];
+                }
+                double sum = 0.0;
+                for (int j = 0; j < nv; ++j) sum += exp(s[j] - m);
+                for (int j = 0; j < nv; ++j) {
+                    double pj = exp(s[j] - m) / sum;
+                    const double* vj = v + (((size_t)b * nk_max + j) * H + h) * d;
+                    for (int c = 0; c < d; ++c) ot[c] += pj * vj[c];
+                }
+                lse[((size_t)b * nq + t) * H + h] = m + log(sum);
+            }
+            free(s);
+        }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -500,3 +500,47 @@ def test_block_mask_backward_finite_differences(causal):
             fd = (loss(*plus) - loss(*minus)) / (2 * h)
             an = float((grad * delta).sum())
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+# ------------------------------------------------------------ KV-cache decode
+# The decode step (lab write-up, section 6.1): nq new queries at the end of
+# their sequence attend to the cached keys and values.
+
+@pytest.mark.parametrize("nq", [1, 3, 40])
+def test_decode_is_the_last_rows_of_causal_attention(nq):
+    L, H, d = 40, 2, 8
+    q, k, v = rnd((L, H, d), 600), rnd((L, H, d), 601), rnd((L, H, d), 602)
+    o_full, l_full = oracle.forward(q, k, v, scale=0.4, causal=True, N=L)
+    o, lse = oracle.decode(q[None, L - nq:], k[None], v[None], scale=0.4, causal=True)
+    np.testing.assert_allclose(o[0], o_full[L - nq:], atol=1e-13)
+    np.testing.assert_allclose(lse[0], l_full[L - nq:], atol=1e-13)
+
+
+def test_decode_matches_torch_sdpa_fp64():
+    B, H, d, nk, nq = 3, 2, 16, 50, 4
+    q, kc, vc = rnd((B, nq, H, d), 610), rnd((B, nk, H, d), 611), rnd((B, nk, H, d), 612)
+    lens = [50, 17, 4]
+    for causal in (False, True):
+        o, lse = oracle.decode(q, kc, vc, scale=0.3, causal=causal, seqlens_k=lens)
+        for b, L in enumerate(lens):
+            tq, tk, tv = (torch.tensor(x[b]).permute(1, 0, 2) for x in (q, kc[:, :L], vc[:, :L]))
+            mask = None
+            if causal:  # bottom-right: query t sees keys j <= L - nq + t
+                mask = torch.arange(L)[None, :] <= (L - nq + torch.arange(nq))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3)
+            np.testing.assert_allclose(o[b], ref.permute(1, 0, 2).numpy(), atol=1e-12)
+            S = torch.einsum("htd,hjd->htj", tq, tk) * 0.3
+            if mask is not None:
+                S = S.masked_fill(~mask, float("-inf"))
+            np.testing.assert_allclose(lse[b], torch.logsumexp(S, -1).T.numpy(), atol=1e-12)
+
+
+def test_decode_queries_that_see_no_key():
+    # causal with fewer cached keys than new queries: the first queries see nothing
+    B, H, d, nk, nq = 1, 1, 8, 6, 4
+    q, kc, vc = rnd((B, nq, H, d), 620), rnd((B, nk, H, d), 621), rnd((B, nk, H, d), 622)
+    o, lse = oracle.decode(q, kc, vc, scale=0.5, causal=True, seqlens_k=[2])
+    # L - nq + t + 1 = t - 1 keys: t = 0, 1 see none, t = 2 sees key 0, t = 3 keys 0, 1
+    assert np.all(o[0, :2] == 0.0) and np.all(np.isneginf(lse[0, :2]))
+    np.testing.assert_allclose(o[0, 2, 0], vc[0, 0, 0], atol=1e-15)
+    assert np.isclose(lse[0, 2, 0], 0.5 * float(q[0, 2, 0] @ kc[0, 0, 0]), atol=1e-14)
