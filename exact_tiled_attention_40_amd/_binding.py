@@ -21,6 +21,7 @@ FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 FA_MASK_BLOCK = 128       # rows and columns of one block-mask entry
 FA_MASK_MAX_N = 65536     # longest sequence the block-sparse calls accept
+FA_DECODE_MAX_Q = 4       # new query tokens per sequence in one decode step
 _DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 
 
@@ -54,6 +55,10 @@ def _load():
     lib.fa_backward_block_sparse.restype = i
     lib.fa_backward_block_sparse_stage.argtypes = [i] + lib.fa_backward_block_sparse.argtypes
     lib.fa_backward_block_sparse_stage.restype = i
+    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
+    lib.fa_decode.restype = i
     lib.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
     lib.fa_dropout_mask.restype = i
     lib.fa_strerror.argtypes = [i]
@@ -215,3 +220,38 @@ def fa_dropout_mask(b: int, h: int, N: int, dropout_p: float, seed: int, *, out=
         out = torch.empty((N, N), dtype=torch.uint8, device=device)
     _check(_lib.fa_dropout_mask(_ptr(out), b, h, N, float(dropout_p), int(seed) & (2**64 - 1), _stream(stream)))
     return out
+
+
+def fa_decode_workspace_size(B: int, H: int, nq: int, nk_max: int, d: int) -> int:
+    return int(_lib.fa_decode_workspace_size(B, H, nq, nk_max, d))
+
+
+def fa_decode(q, k_cache, v_cache, *, seqlens_k=None, scale=None, causal=False, out=None, lse=None,
+              workspace=None, stream=None):
+    """One KV-cache decode step.  q [B, nq, H, d]; k_cache, v_cache
+    [B, nk_max, H, d] (contiguous); seqlens_k optional int32 [B] on the
+    device.  Returns (o [B, nq, H, d], lse float32 [B, nq, H])."""
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise FAError(3, fa_strerror(3))
+    for t in (q, k_cache, v_cache):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("q, k_cache and v_cache must be contiguous 4-d tensors")
+    B, nq, H, d = q.shape
+    nk = k_cache.shape[1]
+    if tuple(k_cache.shape) != (B, nk, H, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache, v_cache must be [B, nk_max, H, d] with q's B, H, d")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or not seqlens_k.is_cuda or seqlens_k.numel() != B):
+        raise ValueError("seqlens_k must be an int32 device tensor of B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, nq, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, fa_decode_workspace_size(B, H, nq, nk, d)), dtype=torch.uint8,
+                                device=q.device)
+    _check(_lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(out), _ptr(lse), B, H, nq,
+                          nk, d, float(scale), int(bool(causal)), _stream(stream), _DTYPES[q.dtype], _ptr(workspace),
+                          workspace.numel() * workspace.element_size()))
+    return out, lse

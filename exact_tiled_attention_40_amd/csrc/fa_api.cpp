@@ -156,6 +156,37 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
                        dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, block_mask, true);
 }
 
+size_t fa_decode_workspace_size(int B, int H, int nq, int nk_max, int d) {
+  if (B < 1 || H < 1 || nq < 1 || nk_max < 1 || d < 1) return 0;
+  const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)fa::decode_splits(nk_max) * (uint64_t)nq;
+  const uint64_t floats = rows * ((uint64_t)d + 2);
+  if (floats > (UINT64_MAX / 8)) return 0;
+  return (size_t)(floats * 4);
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
+              int B, int H, int nq, int nk_max, int d, float scale, int causal, void* stream, int dtype,
+              void* workspace, size_t workspace_bytes) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_NULL_POINTER;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || nq < 1 || nk_max < 1) return FA_ERR_BAD_SHAPE;
+  if (nq > FA_DECODE_MAX_Q) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * fa::decode_splits(nk_max) > INT32_MAX || (int64_t)B * nq * H > INT32_MAX)
+    return FA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGNMENT;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERR_ALIGNMENT;
+  const size_t need = fa_decode_workspace_size(B, H, nq, nk_max, d);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGNMENT;
+  fa::DecodeShape s{B, H, nq, nk_max, d, causal != 0, dtype == FA_DTYPE_BF16, scale};
+  const hipError_t e = fa::launch_decode(s, q, k_cache, v_cache, seqlens_k, o, lse,
+                                         static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed, void* stream) {
   if (!keep) return FA_ERR_NULL_POINTER;
   if (b < 0 || h < 0 || N < 1 || (int64_t)N * N > ((int64_t)1 << 40)) return FA_ERR_BAD_SHAPE;

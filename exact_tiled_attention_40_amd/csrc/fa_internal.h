@@ -34,6 +34,21 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
 // dK/dV kernel (which reads D).
 constexpr int kBwdDq = 1, kBwdKV = 2, kBwdAll = 3;
 
+// KV-cache decode step: nq new queries per sequence against its cache.
+struct DecodeShape {
+  int B, H, nq, nk, d;  // nk = cache capacity (tokens) per sequence
+  bool causal;
+  bool bf16;
+  float scale;
+};
+
+// Number of 512-key chunks (split workgroups) of a cache of nk tokens.
+int decode_splits(int nk);
+
+// workspace: fp32, B*H*decode_splits(nk)*nq*(d + 2) floats.
+hipError_t launch_decode(const DecodeShape& s, const void* q, const void* k, const void* v, const int32_t* lk,
+                         void* o, float* lse, float* workspace, hipStream_t stream);
+
 hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,
                                hipStream_t stream);
 

@@ -174,6 +174,37 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
                                    void* workspace, size_t workspace_bytes,
                                    const uint8_t* block_mask);
 
+/* ------------------------------------------------------ KV-cache decode
+ * One decode step of inference with a KV cache (lab write-up, section 6.1):
+ * nq new query tokens of each sequence attend to that sequence's cached keys
+ * and values, the new tokens being the last nq positions of the sequence.
+ *   q, o        : [B, nq, H, d] contiguous (o: output, dtype).
+ *   k_cache,
+ *   v_cache     : [B, nk_max, H, d] contiguous; the first seqlens_k[b]
+ *                 tokens of sequence b are valid (all nk_max if seqlens_k is
+ *                 NULL).
+ *   seqlens_k   : DEVICE int32 [B] or NULL; values are clamped to
+ *                 [0, nk_max].
+ *   lse         : output, float32 [B, nq, H] (natural log).
+ *   causal      : query t (0 <= t < nq) sees keys j <= L - nq + t
+ *                 (bottom-right alignment); otherwise every valid key.  A
+ *                 query that sees no key gets O = 0, lse = -inf.
+ *   workspace   : DEVICE memory of fa_decode_workspace_size() bytes, 16-byte
+ *                 aligned, no initialisation needed (fp32 partial results of
+ *                 the 512-key chunks).
+ * 1 <= nq <= FA_DECODE_MAX_Q, d in {64, 128}, nk_max >= 1.  Errors as for
+ * fa_forward (FA_ERR_WORKSPACE for a missing or short workspace).  Enqueues
+ * a split kernel (one workgroup per sequence, head and 512-key chunk) and a
+ * merge kernel (log-sum-exp weighted sum of the chunks, the online-softmax
+ * rule of section 3.2 of the lab write-up). */
+#define FA_DECODE_MAX_Q 4
+
+size_t fa_decode_workspace_size(int B, int H, int nq, int nk_max, int d);
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+              void* o, float* lse, int B, int H, int nq, int nk_max, int d, float scale,
+              int causal, void* stream, int dtype, void* workspace, size_t workspace_bytes);
+
 /* Dropout keep mask of a single (b, h) head as the fused kernels draw it:
  * keep[i * N + j] = 1 if element (i, j) is kept, 0 if dropped, for
  * 0 <= i, j < N (both local indices; causal masking is NOT applied).  keep

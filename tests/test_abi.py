@@ -25,10 +25,10 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage",
-                                    "fa_backward_stage",
-                                    "fa_backward_workspace_size", "fa_dropout_mask", "fa_forward",
-                                    "fa_forward_block_sparse", "fa_strerror"]
+    assert declared_functions() == sorted([
+        "fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage", "fa_backward_stage",
+        "fa_backward_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_dropout_mask", "fa_forward",
+        "fa_forward_block_sparse", "fa_strerror"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -55,6 +55,9 @@ def lib():
     L.fa_forward_block_sparse.argtypes = L.fa_forward.argtypes + [vp]
     L.fa_backward_block_sparse.argtypes = L.fa_backward.argtypes + [vp]
     L.fa_backward_block_sparse_stage.argtypes = [i] + L.fa_backward_block_sparse.argtypes
+    L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_decode_workspace_size.restype = ctypes.c_size_t
+    L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     return L
@@ -170,3 +173,28 @@ def test_block_sparse_backward_rejects_bad_arguments(lib):
     assert lib.fa_backward_block_sparse_stage(2, *stage_args, P) == 4
     assert lib.fa_backward_block_sparse_stage(-1, *stage_args, P) == 4
     assert lib.fa_backward_block_sparse_stage(0, *stage_args, None) == 1
+
+
+# ------------------------------------------------------------ decode
+
+def test_decode_workspace_size(lib):
+    # B * H * ceil(nk / 512) * nq * (d + 2) floats
+    assert lib.fa_decode_workspace_size(2, 3, 4, 1000, 128) == 2 * 3 * 2 * 4 * 130 * 4
+    assert lib.fa_decode_workspace_size(1, 1, 1, 512, 64) == 66 * 4
+    assert lib.fa_decode_workspace_size(0, 1, 1, 512, 64) == 0
+    assert lib.fa_decode_workspace_size(1, 1, 1, 0, 64) == 0
+
+
+def test_decode_rejects_bad_arguments(lib):
+    need = lib.fa_decode_workspace_size(1, 2, 1, 1024, 128)
+
+    def call(q=P, k=P, v=P, lens=None, o=P, lse=P, B=1, H=2, nq=1, nk=1024, d=128, scale=0.1, causal=0, dtype=1,
+             ws=P, wsb=need):
+        return lib.fa_decode(q, k, v, lens, o, lse, B, H, nq, nk, d, scale, causal, None, dtype, ws, wsb)
+    assert call(q=None) == 1 and call(k=None) == 1 and call(lse=None) == 1
+    assert call(B=0) == 2 and call(H=0) == 2 and call(nq=0) == 2 and call(nk=0) == 2
+    assert call(nq=5) == 3 and call(d=32) == 3 and call(d=96) == 3 and call(dtype=7) == 3
+    assert call(scale=float("nan")) == 4 and call(scale=0.0) == 4
+    assert call(q=P + 8) == 5 and call(lse=P + 4) == 5 and call(lens=P + 2) == 5
+    assert call(ws=None) == 6 and call(wsb=need - 1) == 6
+    assert call(ws=P + 4) == 5

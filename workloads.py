@@ -160,3 +160,59 @@ def block_mask(B: int, H: int, N: int, density: float, seed: int, *, block: int 
         idx = torch.arange(nb)
         m[:, :, idx, idx] = 1
     return m
+
+
+# ------------------------------------------------------------ KV-cache decode
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    nq: int                  # new query tokens per sequence
+    nk: int                  # cache capacity per sequence
+    d: int
+    dtype: str
+    causal: bool
+    ragged: bool = False     # valid cache lengths ~ U{1..nk} per sequence (else all nk)
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The lab write-up's inference case (section 6.1): one new token per sequence
+# against a long cache, at its section-5 head shape (32 heads of 128 would be
+# the LLaMA-7B layout of the how-to; 8192 cached tokens).
+DECODE_WORKLOADS = {w.name: w for w in (
+    DecodeWorkload("decode_B8_H32_nq1_Nk8192_d128_bf16", 8, 32, 1, 8192, 128, "bf16", True, seed=1101),
+    DecodeWorkload("decode_B16_H8_nq4_Nk4096_d64_f16_ragged", 16, 8, 4, 4096, 64, "f16", True, ragged=True,
+                   seed=1102),
+)}
+DECODE_HEADLINE = "decode_B8_H32_nq1_Nk8192_d128_bf16"
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    wl: DecodeWorkload
+    q: torch.Tensor          # [B, nq, H, d]
+    k: torch.Tensor          # [B, nk, H, d]
+    v: torch.Tensor
+    seqlens: Optional[torch.Tensor]  # int32 [B] or None
+
+
+def make_decode_inputs(wl: DecodeWorkload, lengths: Optional[Sequence[int]] = None) -> DecodeInputs:
+    """Same recipe as make_inputs: [lengths], q, k_cache, v_cache as fp32
+    normals rounded once to the dtype.  Ragged lengths ~ U{1..nk} unless given."""
+    g = torch.Generator().manual_seed(wl.seed)
+    dt = DTYPES[wl.dtype]
+    seq = None
+    if lengths is not None:
+        seq = torch.tensor(list(lengths), dtype=torch.int32)
+    elif wl.ragged:
+        seq = torch.randint(1, wl.nk + 1, (wl.B,), generator=g).to(torch.int32)
+    q = torch.randn(wl.B, wl.nq, wl.H, wl.d, generator=g).to(dt)
+    k = torch.randn(wl.B, wl.nk, wl.H, wl.d, generator=g).to(dt)
+    v = torch.randn(wl.B, wl.nk, wl.H, wl.d, generator=g).to(dt)
+    return DecodeInputs(wl, q, k, v, seq)
