@@ -2,7 +2,7 @@
 """Attention forward + backward throughput on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--block-density P]
+                    [--block-density P] [--decode]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 fa_forward (fused tiled forward) followed by the two backward kernels
@@ -171,6 +171,79 @@ def pmc_summary(pmc_dir: str, calib_bytes: int) -> int:
     return 0
 
 
+def decode_bench(args) -> int:
+    """One decode step = fa_decode (split kernel + merge kernel) over the
+    workload's caches; HBM-bound, so the roofline is bytes against 8 TB/s.
+    Algorithmic bytes = the valid K and V cache rows read once, plus q, o and
+    lse."""
+    import torch
+    import exact_tiled_attention_40_amd as fa
+    import workloads
+
+    wl = workloads.DECODE_WORKLOADS[args.workload or workloads.DECODE_HEADLINE]
+    x = workloads.make_decode_inputs(wl)
+    dev = torch.device("cuda")
+    q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+    lens = x.seqlens.to(dev) if x.seqlens is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.nq, wl.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_decode_workspace_size(wl.B, wl.H, wl.nq, wl.nk, wl.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fa_decode(q, k, v, seqlens_k=lens, scale=wl.scale, causal=wl.causal, out=o, lse=lse, workspace=ws,
+                     stream=stream)
+
+    t_settle = time.perf_counter()
+    while True:
+        for _ in range(max(args.warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_settle >= args.settle_s:
+            break
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    valid = int(x.seqlens.clamp(0, wl.nk).sum()) if x.seqlens is not None else wl.B * wl.nk
+    esz = 2
+    kv_bytes = 2 * valid * wl.H * wl.d * esz
+    io_bytes = wl.B * wl.nq * wl.H * (2 * wl.d * esz + 4)
+    algo = kv_bytes + io_bytes
+    gbs = algo / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "KV-cache decode step GB/s (cache bytes read, % of HBM peak)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "nq": wl.nq, "nk": wl.nk, "d": wl.d,
+                   "causal": wl.causal, "valid_cache_tokens": valid},
+        "roofline": {"bound": "hbm", "kernel": "fa_decode (split + merge)", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": ms,
+                     "algorithmic_bytes_per_launch": algo},
+        "wall_s_timed": wall,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        qd, kd, vd = (t.double().numpy() for t in (x.q, x.k, x.v))
+        t1 = time.perf_counter()
+        oracle.decode(qd, kd, vd, scale=wl.scale, causal=wl.causal,
+                      seqlens_k=None if x.seqlens is None else x.seqlens.numpy())
+        sec = time.perf_counter() - t1
+        line["cpu_baseline"] = {"value": algo / sec / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+                                "kind": "oracle", "seconds": sec,
+                                "sample": "the whole decode step of the workload, fp64 (bytes counted as the "
+                                          "kernel's 16-bit cache bytes)"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +259,8 @@ def main() -> int:
     ap.add_argument("--block-density", type=float, default=0.0,
                     help="time the block-sparse calls with a random 128x128 block mask of this density "
                          "(diagonal blocks kept); 0 = dense")
+    ap.add_argument("--decode", action="store_true",
+                    help="time fa_decode (KV-cache decode step) on a decode workload instead")
     ap.add_argument("--settle-s", type=float, default=1.5,
                     help="repeat the warm-up steps until this many seconds have passed (clock settling)")
     args = ap.parse_args()
@@ -198,6 +273,9 @@ def main() -> int:
         return copy_calibration(args.copy_bytes, args.steps)
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary, args.calib_bytes)
+
+    if args.decode:
+        return decode_bench(args)
 
     import torch
     import exact_tiled_attention_40_amd as fa

@@ -5,7 +5,7 @@
 // The step reads every cached key and value once and does O(d) work per
 // byte, so it is HBM-bound: no matrix cores, and the design is about keeping
 // enough coalesced 16-byte loads in flight on every CU.
-//   - Split-KV: one workgroup per (sequence, head, 512-key chunk), so even a
+//   - Split-KV: one workgroup per (sequence, head, 1024-key chunk), so even a
 //     single sequence fills the 256 CUs.  Lanes take 16-byte slices of key
 //     rows (d/8 lanes per row), reduce the partial dot products across the
 //     row with shuffles, and keep the chunk's scores in LDS; the chunk's max
@@ -22,8 +22,8 @@ namespace fa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecChunk = 512;  // keys per split workgroup
-constexpr int kDecBatch = 4;    // key rows each lane has in flight per tensor
+constexpr int kDecChunk = 1024;  // keys per split workgroup
+constexpr int kDecBatch = 8;     // key rows each lane has in flight per tensor
 
 struct DecArgs {
   const uint16_t* q;  // [B, nq, H, d]
@@ -237,11 +237,11 @@ __global__ __launch_bounds__(64) void fa_decode_merge_kernel(DecArgs a) {
 #pragma unroll
   for (int e = 0; e < kE; ++e) o[e] = 0.f;
   if (M != -INFINITY) {
+    // a chunk with no visible key has m = -inf, l = 0 and O = 0: weight 0
+#pragma unroll 4
     for (int s = 0; s < a.nsplit; ++s) {
       const int64_t p = (bh * a.nsplit + s) * a.nq + t;
-      const float ms = a.part_m[p];
-      if (ms == -INFINITY) continue;  // a chunk with no visible key
-      const float f = __builtin_amdgcn_exp2f(ms - M);
+      const float f = __builtin_amdgcn_exp2f(a.part_m[p] - M);
       Lsum += a.part_l[p] * f;
 #pragma unroll
       for (int e = 0; e < kE; ++e) o[e] += a.part_o[p * D + lane + 64 * e] * f;

@@ -42,7 +42,7 @@ struct DecodeShape {
   float scale;
 };
 
-// Number of 512-key chunks (split workgroups) of a cache of nk tokens.
+// Number of 1024-key chunks (split workgroups) of a cache of nk tokens.
 int decode_splits(int nk);
 
 // workspace: fp32, B*H*decode_splits(nk)*nq*(d + 2) floats.

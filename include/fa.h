@@ -191,10 +191,10 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
  *                 query that sees no key gets O = 0, lse = -inf.
  *   workspace   : DEVICE memory of fa_decode_workspace_size() bytes, 16-byte
  *                 aligned, no initialisation needed (fp32 partial results of
- *                 the 512-key chunks).
+ *                 the 1024-key chunks).
  * 1 <= nq <= FA_DECODE_MAX_Q, d in {64, 128}, nk_max >= 1.  Errors as for
  * fa_forward (FA_ERR_WORKSPACE for a missing or short workspace).  Enqueues
- * a split kernel (one workgroup per sequence, head and 512-key chunk) and a
+ * a split kernel (one workgroup per sequence, head and 1024-key chunk) and a
  * merge kernel (log-sum-exp weighted sum of the chunks, the online-softmax
  * rule of section 3.2 of the lab write-up). */
 #define FA_DECODE_MAX_Q 4

@@ -178,8 +178,9 @@ def test_block_sparse_backward_rejects_bad_arguments(lib):
 # ------------------------------------------------------------ decode
 
 def test_decode_workspace_size(lib):
-    # B * H * ceil(nk / 512) * nq * (d + 2) floats
-    assert lib.fa_decode_workspace_size(2, 3, 4, 1000, 128) == 2 * 3 * 2 * 4 * 130 * 4
+    # B * H * ceil(nk / 1024) * nq * (d + 2) floats
+    assert lib.fa_decode_workspace_size(2, 3, 4, 1000, 128) == 2 * 3 * 1 * 4 * 130 * 4
+    assert lib.fa_decode_workspace_size(2, 3, 4, 1025, 128) == 2 * 3 * 2 * 4 * 130 * 4
     assert lib.fa_decode_workspace_size(1, 1, 1, 512, 64) == 66 * 4
     assert lib.fa_decode_workspace_size(0, 1, 1, 512, 64) == 0
     assert lib.fa_decode_workspace_size(1, 1, 1, 0, 64) == 0
