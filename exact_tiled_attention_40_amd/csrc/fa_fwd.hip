@@ -2,7 +2,9 @@
 //
 // One workgroup = one (batch-or-sequence b, head h, block of kBR queries);
 // eight waves (two per SIMD, so one wave's softmax overlaps the other's
-// matrix products), each owning 32 consecutive queries.  The kernel walks the
+// matrix products), each owning 32 consecutive queries.  The block-sparse
+// instantiation uses four waves (128 queries, one mask row) and two
+// workgroups per CU instead.  The kernel walks the
 // key blocks the block needs (all of them, or only those left of the
 // diagonal when causal), which is the tiling of the lab write-up
 // "FlashAttention" (dpshk.com), section 3.1, with QK^T, softmax and PV fused
@@ -33,9 +35,11 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 8;  // two per SIMD; 256 queries share each K/V tile
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBR = 32 * kWaves;  // queries per workgroup
+// Dense: eight waves (two per SIMD, ping-pong), 256 queries share each K/V
+// tile.  Block-sparse: four waves (one 128-query mask row per workgroup, so
+// the tile list is exact), two workgroups per CU, no ping-pong.
+template <bool SPARSE> constexpr int waves() { return SPARSE ? 4 : 8; }
+template <bool SPARSE> constexpr int rows_per_wg() { return 32 * waves<SPARSE>(); }
 constexpr int kBC = 64;           // keys per tile
 // The partial output is rescaled only when a row max grows by more than this
 // many powers of two; otherwise the stale max stays the reference, so the
@@ -61,8 +65,10 @@ struct FwdArgs {
 };
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
-__global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_kernel(FwdArgs a) {
   using T = MTile<D, kBC>;
+  constexpr int kWaves = waves<SPARSE>();
+  constexpr int kBR = rows_per_wg<SPARSE>();
   constexpr int kNS = 2 * (D / 16);  // S^T products per tile (two 32-key tiles x D/16 k-steps)
   constexpr int kNO = 4 * (D / 32);  // O^T products per tile (four 16-key slices x D/32 tiles)
   constexpr int kPF = 3;             // LDS operand reads in flight (products ahead)
@@ -71,11 +77,12 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   // partial), and tile loads per wave per tile step
   constexpr int kPer = (T::kBlocks + kWaves - 1) / kWaves;
   constexpr int kLoads = 2 * kPer;
-  static_assert(kLoads == 2 || kLoads == 4, "load spreading assumes 2 or 4 loads per step");
+  static_assert(SPARSE || kLoads == 2 || kLoads == 4, "softmax-phase load spreading assumes 2 or 4 loads");
+  static_assert(kNS % kLoads == 0 && kNS / kLoads >= 2, "product-phase load spreading");
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
-  // block-sparse: the key tiles the workgroup visits (in order) and which of
-  // its two 128-query mask rows each one serves
+  // block-sparse: the key tiles the workgroup visits (in order; the flags
+  // are all 1: one mask row per workgroup)
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];
   __shared__ uint8_t tflag[SPARSE ? kMaxSparseTiles : 1];
   __shared__ int tcount[SPARSE ? 1 : 1];
@@ -346,9 +353,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
   if constexpr (SPARSE) {
     if (w == 0) {
       const uint8_t* mrow = a.bmask + ((int64_t)b * a.H + h) * a.nb * a.nb;
-      const int r0 = q0 / kMaskBlock;
-      const int n = build_tile_list(mrow + (int64_t)r0 * a.nb, r0 + 1 < a.nb ? mrow + (int64_t)(r0 + 1) * a.nb : nullptr,
-                                    0, 1, ntiles, tlist, tflag, lane);
+      static_assert(!SPARSE || kBR == kMaskBlock, "one mask row per block-sparse workgroup");
+      const int n = build_tile_list(mrow + (int64_t)(q0 / kMaskBlock) * a.nb, nullptr, 0, 1, ntiles, tlist, tflag,
+                                    lane);
       if (lane == 0) tcount[0] = n;
     }
     __syncthreads();
@@ -358,11 +365,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(tlist[k]);
     else return k;
   };
-  const int grp = w / (kWaves / 2);  // also the wave's 128-query mask row in the workgroup
-  auto skip_at = [&](int k) __attribute__((always_inline)) -> bool {
-    if constexpr (SPARSE) return ((__builtin_amdgcn_readfirstlane(tflag[k]) >> grp) & 1) == 0;
-    else return false;
-  };
+  // ping-pong group (dense); the block-sparse workgroup runs every wave as
+  // group 0 (no phase offset)
+  const int grp = SPARSE ? 0 : w / (kWaves / 2);
+  auto skip_at = [&](int) __attribute__((always_inline)) -> bool { return false; };
 
   if (n_list > 0) {
     issue(kbase, ks0, tile_at(0) * kBC);
@@ -464,23 +470,26 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdArgs a) {
 }
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
-hipError_t launch_fwd_t(const FwdArgs& args, int nblocks, hipStream_t stream) {
-  if (args.bmask)
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, true>), dim3(nblocks), dim3(kThreads), 0,
-                       stream, args);
+hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
+  const bool sparse = args.bmask != nullptr;
+  const int64_t nblocks = (int64_t)args.nqb * args.B * args.H;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (sparse)
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, true>), dim3((unsigned)nblocks),
+                       dim3(64 * waves<true>()), 0, stream, args);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, false>), dim3(nblocks), dim3(kThreads), 0,
-                       stream, args);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, false>), dim3((unsigned)nblocks),
+                       dim3(64 * waves<false>()), 0, stream, args);
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
-hipError_t launch_fwd_d(const AttnShape& s, const FwdArgs& args, int nblocks, hipStream_t stream) {
+hipError_t launch_fwd_d(const AttnShape& s, const FwdArgs& args, hipStream_t stream) {
   if (s.causal)
-    return s.dropout ? launch_fwd_t<D, BF16, true, true>(args, nblocks, stream)
-                     : launch_fwd_t<D, BF16, true, false>(args, nblocks, stream);
-  return s.dropout ? launch_fwd_t<D, BF16, false, true>(args, nblocks, stream)
-                   : launch_fwd_t<D, BF16, false, false>(args, nblocks, stream);
+    return s.dropout ? launch_fwd_t<D, BF16, true, true>(args, stream)
+                     : launch_fwd_t<D, BF16, true, false>(args, stream);
+  return s.dropout ? launch_fwd_t<D, BF16, false, true>(args, stream)
+                   : launch_fwd_t<D, BF16, false, false>(args, stream);
 }
 
 // Dropout keep mask of one head, N x N bytes: one thread per 4 consecutive
@@ -513,7 +522,8 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
   a.B = s.B;
   a.H = s.H;
   a.N = s.N;
-  a.nqb = (s.N + kBR - 1) / kBR;
+  const int br = s.bmask ? rows_per_wg<true>() : rows_per_wg<false>();
+  a.nqb = (s.N + br - 1) / br;
   a.scale_log2 = s.scale * kLog2e;
   a.drop_thresh = s.drop_thresh;
   a.drop_rescale = s.drop_rescale;
@@ -521,17 +531,15 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
   a.seed_hi = (uint32_t)(s.seed >> 32);
   a.bmask = s.bmask;
   a.nb = s.nb;
-  const int64_t nblocks = (int64_t)a.nqb * s.B * s.H;
-  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   switch (s.d) {
-    case 32: return s.bf16 ? launch_fwd_d<32, true>(s, a, (int)nblocks, stream)
-                           : launch_fwd_d<32, false>(s, a, (int)nblocks, stream);
-    case 64: return s.bf16 ? launch_fwd_d<64, true>(s, a, (int)nblocks, stream)
-                           : launch_fwd_d<64, false>(s, a, (int)nblocks, stream);
-    case 96: return s.bf16 ? launch_fwd_d<96, true>(s, a, (int)nblocks, stream)
-                           : launch_fwd_d<96, false>(s, a, (int)nblocks, stream);
-    default: return s.bf16 ? launch_fwd_d<128, true>(s, a, (int)nblocks, stream)
-                           : launch_fwd_d<128, false>(s, a, (int)nblocks, stream);
+    case 32: return s.bf16 ? launch_fwd_d<32, true>(s, a, stream)
+                           : launch_fwd_d<32, false>(s, a, stream);
+    case 64: return s.bf16 ? launch_fwd_d<64, true>(s, a, stream)
+                           : launch_fwd_d<64, false>(s, a, stream);
+    case 96: return s.bf16 ? launch_fwd_d<96, true>(s, a, stream)
+                           : launch_fwd_d<96, false>(s, a, stream);
+    default: return s.bf16 ? launch_fwd_d<128, true>(s, a, stream)
+                           : launch_fwd_d<128, false>(s, a, stream);
   }
 }
 
