@@ -198,6 +198,8 @@ __global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_k
   // order inside each 16-key slice is permuted and V^T is read with the
   // same permutation).
   auto m_phase = [&](int t, bool do_s, auto&& hook) __attribute__((always_inline)) {
+    // the matrix phase issues ahead of the other group's softmax on the SIMD
+    __builtin_amdgcn_s_setprio(1);
     if (do_s) {
       uint32_t k0 = ks0 + ((t + 1) & 1) * T::kBytes + ob0, k1 = ks0 + ((t + 1) & 1) * T::kBytes + ob1;
       uint32_t v0 = vs0 + (t & 1) * T::kBytes + tb0, v1 = vs0 + (t & 1) * T::kBytes + tb1;
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_k
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Vector phase of tile t: mask, online softmax of sacc (register r of key
