@@ -585,7 +585,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   using T = MTile<D, kBR>;
-  constexpr int kNB = 3;  // Q/dO/LSE/D tile buffers
+  constexpr int kNB = 4;  // Q/dO/LSE/D tile buffers
   __shared__ __attribute__((aligned(1024))) uint16_t qs[kNB][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t gs[kNB][T::kElems];
   __shared__ __attribute__((aligned(16))) float ls[kNB][kBR];
@@ -704,10 +704,51 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   };
   const int t_first = n_list > 0 ? tile_at(0) : 0;
 
+  // Loads of visited tile tkl (-1: none) into buffer lbuf, as one wave's
+  // share: part k < 2 * kNU is a Q (even) or dO (odd) block, part 2 * kNU
+  // the LSE (wave 0) or D (wave 1) row; waves 2 and 3 send an empty load to
+  // a spare row, so every wave issues kTileLoads loads per tile.  An absent
+  // tile has empty buffer ranges: its loads fetch nothing and fill the
+  // buffer with zeros.
+  constexpr int kNU = T::kBlocks / kWaves;  // blocks per tensor per wave
+  constexpr int kTileLoads = 2 * kNU + 1;
+  struct TileLoads {
+    __amdgpu_buffer_rsrc_t qr, gr, xr;
+    uint32_t qdst, gdst, xdst;
+  };
+  const uint32_t xoff = (uint32_t)lane * hstride4;
+  auto tile_loads = [&](int tkl, int lbuf) __attribute__((always_inline)) {
+    const int il = i_begin + max(tkl, 0) * kBR;
+    const int rows = tkl >= 0 ? min(kBR, L - il) : 0;
+    const int64_t tok = min(il, L - 1);
+    TileLoads x;
+    x.qr = make_rsrc(qbase + tok * ld, rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u);
+    x.gr = make_rsrc(gbase + tok * hd, rows > 0 ? (uint32_t)(rows - 1) * grow_bytes + D * 2 : 0u);
+    x.xr = w < 2 ? make_rsrc((w == 0 ? lbase : dbase) + tok * a.H, rows > 0 ? (uint32_t)(rows - 1) * a.H * 4 + 4 : 0u)
+                 : make_rsrc(nullptr, 0u);
+    x.qdst = qs0 + lbuf * T::kBytes;
+    x.gdst = gs0 + lbuf * T::kBytes;
+    x.xdst = w == 0 ? ls0 + lbuf * kBR * 4 : w == 1 ? dls0 + lbuf * kBR * 4 : lds_addr(spare);
+    return x;
+  };
+  auto tile_load_part = [&](const TileLoads& x, int k) __attribute__((always_inline)) {
+    if (k == 2 * kNU)
+      buffer_load_lds4_addr(x.xr, x.xdst, xoff);
+    else if (k & 1)
+      T::load(x.gr, x.gdst, grow_bytes, (k >> 1) * kWaves + w, lane);
+    else
+      T::load(x.qr, x.qdst, row_bytes, (k >> 1) * kWaves + w, lane);
+  };
+
   if (n_list > 0) issue_tile(i_begin + t_first * kBR, 0);
   if (n_list > 1) issue_tile(i_begin + tile_at(1) * kBR, 1);
   wait_vmem();
   __syncthreads();
+  {
+    const TileLoads x = tile_loads(n_list > 2 ? tile_at(2) : -1, 2);
+#pragma unroll
+    for (int k = 0; k <= 2 * kNU; ++k) tile_load_part(x, k);
+  }
 
   // pipeline prologue: S, dP and elements 0..7 of the first half, and the
   // first operands of its look-ahead products (half 1 of tile 0)
@@ -740,46 +781,27 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // Iteration at position t of the visited tiles (tiles tk, tk1, tk2 at
-  // positions t, t+1, t+2; -1 past the end).
-  auto iteration = [&](int t, int tk, int tk1, int tk2, auto mask) {
+  // Iteration at position t of the visited tiles (tiles tk, tk1, tk3 at
+  // positions t, t+1, t+3; -1 past the end).
+  auto iteration = [&](int t, int tk, int tk1, int tk3, auto mask) {
     constexpr bool kMask = decltype(mask)::value;
     const int buf = t % kNB;
     const int nbuf = (t + 1) % kNB;
     const int i0 = i_begin + tk * kBR;
-    // tile t + 1 has landed; every wave is done with tile t - 1's buffers
-    // (the reads still in flight here touch tiles t and t + 1 only)
-    wait_vmem();
+    // tile t + 1 has landed (loads complete in order: only tile t + 2's may
+    // still be in flight); every wave is done with tile t - 1's buffers (the
+    // reads still in flight here touch tiles t and t + 1 only)
+    wait_vmem_n<kTileLoads>();
     barrier_keep_lds_reads();
 
-    // Loads of tile t + 2 into buffer (t + 2) % kNB, spread over the first
-    // half's look-ahead products: Q and dO blocks at even products, LSE or D
-    // (waves 0 and 1) at product 1.  Past the last tile the buffer ranges
-    // are empty: the loads fetch nothing and fill the free buffer with zeros.
-    const int i2 = i_begin + max(tk2, 0) * kBR;
-    const int rows = tk2 >= 0 ? min(kBR, L - i2) : 0;
-    const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc(qbase + (int64_t)min(i2, L - 1) * ld, rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u);
-    const __amdgpu_buffer_rsrc_t gr =
-        make_rsrc(gbase + (int64_t)min(i2, L - 1) * hd, rows > 0 ? (uint32_t)(rows - 1) * grow_bytes + D * 2 : 0u);
-    const __amdgpu_buffer_rsrc_t xr =
-        make_rsrc((w == 0 ? lbase : dbase) + (int64_t)min(i2, L - 1) * a.H,
-                  rows > 0 ? (uint32_t)(rows - 1) * a.H * 4 + 4 : 0u);
-    const int lbuf = (t + 2) % kNB;
-    // waves 2 and 3 send their (empty) LSE/D load to a spare row
-    const uint32_t xdst = w == 0 ? ls0 + lbuf * kBR * 4 : w == 1 ? dls0 + lbuf * kBR * 4 : lds_addr(spare);
-    const uint32_t qdst = qs0 + lbuf * T::kBytes, gdst = gs0 + lbuf * T::kBytes;
-    const uint32_t xoff = (uint32_t)lane * hstride4;
-    auto load_hook = [=](int i) {
-      constexpr int kNU = T::kBlocks / kWaves;  // blocks per tensor per wave
-      if (i % 2 == 0 && i / 2 < 2 * kNU) {
-        const int k = i / 2;
-        if (k & 1)
-          T::load(gr, gdst, grow_bytes, (k >> 1) * kWaves + w, lane);
-        else
-          T::load(qr, qdst, row_bytes, (k >> 1) * kWaves + w, lane);
-      }
-      if (i == 1) buffer_load_lds4_addr(w < 2 ? xr : make_rsrc(nullptr, 0u), xdst, xoff);
+    // Loads of tile t + 3 into buffer (t + 3) % kNB (tile t - 1's), spread
+    // over the first half's look-ahead products: Q and dO blocks at even
+    // products, LSE or D at product 1.
+    const TileLoads x = tile_loads(tk3, (t + 3) % kNB);
+    static_assert(4 * kNU - 2 < D / 8, "the look-ahead products must carry every tile load");
+    auto load_hook = [&](int i) __attribute__((always_inline)) {
+      if (i % 2 == 0 && i / 2 < 2 * kNU) tile_load_part(x, i / 2);
+      if (i == 1) tile_load_part(x, 2 * kNU);
     };
     auto no_hook = [](int) {};
 
@@ -805,18 +827,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   int t = 0;
   int tk = n_list > 0 ? t_first : -1;
   int tk1 = n_list > 1 ? tile_at(1) : -1;
+  int tk2 = n_list > 2 ? tile_at(2) : -1;
   if (CAUSAL)
     for (; t < n_list && tk < 2; ++t) {
-      const int tk2 = t + 2 < n_list ? tile_at(t + 2) : -1;
-      iteration(t, tk, tk1, tk2, std::true_type{});
+      const int tk3 = t + 3 < n_list ? tile_at(t + 3) : -1;
+      iteration(t, tk, tk1, tk3, std::true_type{});
       tk = tk1;
       tk1 = tk2;
+      tk2 = tk3;
     }
   for (; t < n_list; ++t) {
-    const int tk2 = t + 2 < n_list ? tile_at(t + 2) : -1;
-    iteration(t, tk, tk1, tk2, std::false_type{});
+    const int tk3 = t + 3 < n_list ? tile_at(t + 3) : -1;
+    iteration(t, tk, tk1, tk3, std::false_type{});
     tk = tk1;
     tk1 = tk2;
+    tk2 = tk3;
   }
 
 #pragma unroll
@@ -827,7 +852,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 
   // ---- epilogue: dK = scale * dK, dV, staged through LDS as [key][d] rows
   // (register r of tile dt: key 8*(r/4) + 4*h2 + r%4 of the wave, element
-  // dt*32 + l32), then written back 16 bytes per lane.
+  // dt*32 + l32), then written back 16 bytes per lane.  The (empty) loads
+  // of the last iterations still write the tile buffers: wait for them.
+  wait_vmem();
   __syncthreads();
   constexpr int kRowE = D + 8;  // padded LDS row, 16-bit elements
   uint16_t* stage_k = qs[0];    // 128 rows x kRowE elements fit in each set of tile buffers

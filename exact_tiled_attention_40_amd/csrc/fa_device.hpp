@@ -272,6 +272,13 @@ struct MTile {
 // Wait until this wave's outstanding vector-memory operations (including
 // direct-to-LDS loads) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (loads complete in issue order, so the older ones are done).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Workgroup barrier without the LDS fence of __syncthreads(), for loops whose
 // only LDS writes are direct-to-LDS loads (completed by wait_vmem() before
