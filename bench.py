@@ -282,9 +282,6 @@ def main() -> int:
     import workloads
 
     wl = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
-    if wl.varlen:
-        print("bench.py times the fixed-length workloads", file=sys.stderr)
-        return 2
     x = workloads.make_inputs(wl)
     dev = torch.device("cuda")
     if x.qkv is not None:
@@ -300,6 +297,12 @@ def main() -> int:
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     ws = torch.empty(fa.fa_backward_workspace_size(wl.B, wl.N, wl.H, wl.d), dtype=torch.uint8, device=dev)
     kw = dict(scale=wl.scale, causal=wl.causal, dropout_p=wl.dropout_p, seed=wl.seed)
+    if wl.varlen:
+        # packed [total, H, d] tokens of B sequences of the drawn lengths
+        kw.update(cu_seqlens=x.cu_seqlens.to(dev), max_seqlen=wl.N)
+        if args.block_density > 0:
+            print("block masks are timed on the fixed-length workloads", file=sys.stderr)
+            return 2
     stream = torch.cuda.current_stream()
     bm = None
     if args.block_density > 0:
@@ -335,7 +338,7 @@ def main() -> int:
     ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
     step_ms = events[0][0].elapsed_time(events[-1][3]) / args.steps
 
-    pairs = visible_pairs(wl) if bm is None else visible_pairs_masked(wl, bm.numpy())
+    pairs = visible_pairs(wl, x.lengths) if bm is None else visible_pairs_masked(wl, bm.numpy())
     fwd_flops = 4.0 * wl.d * pairs
     bwd_flops = 10.0 * wl.d * pairs
     total_tflops = (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
@@ -354,7 +357,9 @@ def main() -> int:
     dom = max(names, key=lambda n: ms[n])
     achieved = algo_flops[dom] / (ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_TFLOPS, "traffic": measured_traffic(dom),
+                "frac": achieved / PEAK_TFLOPS,
+                # the traffic file holds the counters of the default workload's dense kernels
+                "traffic": measured_traffic(dom) if wl.name == workloads.HEADLINE and bm is None else None,
                 "avg_launch_ms": ms[dom], "algorithmic_flops_per_launch": algo_flops[dom]}
     per_kernel = {n: {"ms": ms[n], "algorithmic_tflops": algo_flops[n] / (ms[n] * 1e-3) / 1e12,
                       "issued_mfma_tflops": issued_flops[n] / (ms[n] * 1e-3) / 1e12} for n in names}
@@ -376,7 +381,9 @@ def main() -> int:
                    "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
                    "dropout_p": wl.dropout_p, "packed_qkv": wl.packed,
                    **({"block_density": args.block_density, "mask_blocks_on": int(bm.sum()),
-                       "mask_blocks": int(bm.numel()), "visible_pairs": pairs} if bm is not None else {})},
+                       "mask_blocks": int(bm.numel()), "visible_pairs": pairs} if bm is not None else {}),
+                   **({"varlen": True, "total_tokens": int(sum(x.lengths)), "visible_pairs": pairs}
+                      if wl.varlen else {})},
         "frac_of_peak": total_tflops / PEAK_TFLOPS,
         "fwd": {"tflops": fwd_tflops, "ms": ms["fa_fwd_kernel"], "frac": fwd_tflops / PEAK_TFLOPS},
         "bwd": {"tflops": bwd_tflops, "ms": bwd_ms, "frac": bwd_tflops / PEAK_TFLOPS},
@@ -385,9 +392,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if bm is not None:
-        line["roofline"]["traffic"] = None  # the traffic file covers the dense kernels
-    if not args.no_cpu_baseline and bm is None:
+    if not args.no_cpu_baseline and bm is None and not wl.varlen:
         line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_heads)
     print(json.dumps(line), flush=True)
     return 0

@@ -87,14 +87,6 @@ __device__ __forceinline__ void seq_range(const BwdArgs& a, int b, int& start, i
   }
 }
 
-// Keep factor of element (query i, key j) of head (b, h): 1/(1-p) if kept,
-// 0 if dropped (Philox word j mod 4 of counter (i, j/4, h, b)).
-__device__ __forceinline__ float keep_factor(const BwdArgs& a, int b, int h, int i, int j) {
-  const Philox4 r = philox4x32_10((uint32_t)i, (uint32_t)j >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
-  const uint32_t w = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
-  return w >= a.drop_thresh ? a.drop_rescale : 0.f;
-}
-
 // ---------------------------------------------------------------- dQ (+ D)
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
 __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
@@ -424,19 +416,53 @@ __device__ __forceinline__ void dkdv_sdp(const KVState<D, BF16>& st, const TileA
 struct HalfCtx {
   uint32_t lb, db;
   int i0, qt;
+  uint32_t kb;  // dropout: bit r set if element r is kept
 };
+
+// Dropout keep bits of this lane's key kj against queries q0 .. q0+3 (bit
+// e: query q0 + e kept).  The four lanes of a quad hold keys 4*(kj/4) ..
+// 4*(kj/4)+3 (lane mod 4 = kj mod 4), whose words for one query come from one
+// Philox block (counter (q, kj/4, h, b)): lane c hashes query q0 + c only, and
+// the quad trades the sixteen comparisons, so each block is computed once.
+__device__ __forceinline__ uint32_t dkdv_keep4(const BwdArgs& a, int b, int h, int q0, int kj) {
+  const int c = kj & 3;
+  const Philox4 r = philox4x32_10((uint32_t)(q0 + c), (uint32_t)kj >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo,
+                                  a.seed_hi);
+  const uint32_t t = a.drop_thresh;
+  uint32_t m = (r.x >= t ? 1u : 0u) | (r.y >= t ? 2u : 0u) | (r.z >= t ? 4u : 0u) | (r.w >= t ? 8u : 0u);
+  m <<= 4 * c;                    // bit 4c + k: query q0 + c, key 4*(kj/4) + k
+  m |= quad_perm<1, 0, 3, 2>(m);
+  m |= quad_perm<2, 3, 0, 1>(m);  // all sixteen bits in every lane of the quad
+  m >>= c;                        // bit 4e: query q0 + e, key kj
+  return (m & 1u) | ((m >> 3) & 2u) | ((m >> 6) & 4u) | ((m >> 9) & 8u);
+}
+
+// Keep bits of this lane's key against the 64 queries of the tile at i0:
+// bit 16*qt + r for element r of half qt (query i0 + 32qt + 8*(r/4) +
+// 4*(lane/32) + r%4).  Computed once per tile in a compact loop, so that the
+// unrolled, software-pipelined loop body stays the size of the dropout-free
+// one.
+__device__ __forceinline__ uint32_t dkdv_tile_keep(const BwdArgs& a, int b, int h, int i0, int h2, int kj) {
+  uint32_t bits = 0;
+#pragma unroll 1
+  for (int g = 0; g < 8; ++g) {
+    const int q0 = i0 + 32 * (g >> 2) + 8 * (g & 3) + 4 * h2;
+    bits |= dkdv_keep4(a, b, h, q0, kj) << (4 * g);
+  }
+  return bits;
+}
 
 // P, Z and dS of element r of a half (register r of S, dP: query
 // 32qt + 8*(r/4) + 4*(lane/32) + r%4 of this lane's key kj).
 template <bool MASK, bool DROPOUT>
 __device__ __forceinline__ void dkdv_elem(const BwdArgs& a, float s, float dp, float lse2, float dd, const HalfCtx& c,
-                                          int r, int kj, int h2, int b, int h, float& z, float& ds) {
+                                          int r, int kj, int h2, float& z, float& ds) {
   const int qi = c.i0 + c.qt * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
   float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, a.scale_log2, -lse2));
   if (MASK && kj > qi) p = 0.f;
   z = p;
   if constexpr (DROPOUT) {
-    const float kfac = keep_factor(a, b, h, qi, kj);
+    const float kfac = (c.kb >> r) & 1u ? a.drop_rescale : 0.f;
     dp *= kfac;
     z = p * kfac;
   }
@@ -466,7 +492,7 @@ template <int D, bool BF16, bool MASK, bool DROPOUT, typename Hook>
 __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st, f32x16& sacc, f32x16& pacc,
                                           uint32_t (&zpk)[8], uint32_t (&spk)[8], u32x4 (&pf)[4],
                                           const TileAddr& nop, const TileAddr& nnop, int nnqt, const TileAddr& tr,
-                                          const HalfCtx& cur, const HalfCtx& nxt, int kj, int h2, int b, int h,
+                                          const HalfCtx& cur, const HalfCtx& nxt, int kj, int h2,
                                           Hook&& hook) {
   using T = MTile<D, kBR>;
   constexpr int kNP = D / 8;  // look-ahead products (S and dP, D/16 k-steps each)
@@ -523,7 +549,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
       const f32x4& l4 = r < 12 ? l4a : l4b;
       const f32x4& d4 = r < 12 ? d4a : d4b;
       float z, ds;
-      dkdv_elem<MASK, DROPOUT>(a, sacc[r], pacc[r], l4[r & 3], d4[r & 3], cur, r, kj, h2, b, h, z, ds);
+      dkdv_elem<MASK, DROPOUT>(a, sacc[r], pacc[r], l4[r & 3], d4[r & 3], cur, r, kj, h2, z, ds);
       if (r & 1) {
         zpk[r >> 1] = pack2<BF16>(zprev, z);
         spk[r >> 1] = pack2<BF16>(dsprev, ds);
@@ -566,7 +592,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
         const f32x4& l4 = r < 4 ? l4c : l4d;
         const f32x4& d4 = r < 4 ? d4c : d4d;
         float z, ds;
-        dkdv_elem<MASK, DROPOUT>(a, ns[r], np[r], l4[r & 3], d4[r & 3], nxt, r, kj, h2, b, h, z, ds);
+        dkdv_elem<MASK, DROPOUT>(a, ns[r], np[r], l4[r & 3], d4[r & 3], nxt, r, kj, h2, z, ds);
         if (r & 1) {
           zpk[r >> 1] = pack2<BF16>(zprev, z);
           spk[r >> 1] = pack2<BF16>(dsprev, ds);
@@ -752,6 +778,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 
   // pipeline prologue: S, dP and elements 0..7 of the first half, and the
   // first operands of its look-ahead products (half 1 of tile 0)
+  // dropout keep bits of the tile in use (bit 16*half + element)
+  uint32_t kb_cur = 0;
+  if constexpr (DROPOUT) kb_cur = dkdv_tile_keep(a, b, h, i_begin + t_first * kBR, h2, kj);
   f32x16 sacc, pacc;
   uint32_t zpk[8], spk[8];
   u32x4 pf[4];
@@ -764,13 +793,13 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     pf[i] = lds_read16_at(base + T::opnd_off(1, s));
   }
   {
-    const HalfCtx c0{ls0 + 16 * h2, dls0 + 16 * h2, i_begin + t_first * kBR, 0};
+    const HalfCtx c0{ls0 + 16 * h2, dls0 + 16 * h2, i_begin + t_first * kBR, 0, kb_cur & 0xffffu};
     float zprev = 0.f, dsprev = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const f32x4 l4 = lds_f32x4(c0.lb + 4 * 8 * (r >> 2)), d4 = lds_f32x4(c0.db + 4 * 8 * (r >> 2));
       float z, ds;
-      dkdv_elem<CAUSAL, DROPOUT>(a, sacc[r], pacc[r], l4[r & 3], d4[r & 3], c0, r, kj, h2, b, h, z, ds);
+      dkdv_elem<CAUSAL, DROPOUT>(a, sacc[r], pacc[r], l4[r & 3], d4[r & 3], c0, r, kj, h2, z, ds);
       if (r & 1) {
         zpk[r >> 1] = pack2<BF16>(zprev, z);
         spk[r >> 1] = pack2<BF16>(dsprev, ds);
@@ -812,15 +841,20 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     uint32_t lb = ls0 + buf * kBR * 4 + 16 * h2, db = dls0 + buf * kBR * 4 + 16 * h2;
     uint32_t nlb = ls0 + nbuf * kBR * 4 + 16 * h2, ndb = dls0 + nbuf * kBR * 4 + 16 * h2;
     asm volatile("" : "+v"(lb), "+v"(db), "+v"(nlb), "+v"(ndb));
-    const HalfCtx h0{lb, db, i0, 0}, h1{lb, db, i0, 1}, n0{nlb, ndb, i_begin + max(tk1, 0) * kBR, 0};
+    // keep bits of the next tile, whose first half the look-ahead reaches
+    uint32_t kb_next = 0;
+    if constexpr (DROPOUT) kb_next = dkdv_tile_keep(a, b, h, i_begin + max(tk1, 0) * kBR, h2, kj);
+    const HalfCtx h0{lb, db, i0, 0, kb_cur & 0xffffu}, h1{lb, db, i0, 1, kb_cur >> 16},
+        n0{nlb, ndb, i_begin + max(tk1, 0) * kBR, 0, kb_next & 0xffffu};
     // On the last tile the look-ahead work reads a stale buffer and is
     // discarded; doing it anyway keeps the tile one basic block.  Masked
     // tiles come first, so the look-ahead into the next tile may use this
     // tile's masking.
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj, h2, b, h,
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj, h2,
                                        load_hook);
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2, b, h,
+    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2,
                                        no_hook);
+    kb_cur = kb_next;
   };
   // Causal: only the first two tiles (queries j0 .. j0+127) hold queries
   // before some key of the block, so only they are masked.

@@ -308,6 +308,13 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// Value of lane 4*(l/4) + Pk in lane l (k = l mod 4): a DPP quad
+// permutation (every lane of the quad must be active).
+template <int P0, int P1, int P2, int P3>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, P0 | (P1 << 2) | (P2 << 4) | (P3 << 6), 0xf, 0xf, false);
+}
+
 // Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
 // multiply-xor round function with a Weyl-sequence key schedule.
 struct Philox4 {
