@@ -37,7 +37,7 @@ int check_common(int B, int H, int N, int d, float scale, float dropout_p, int d
   s->bf16 = dtype == FA_DTYPE_BF16;
   s->scale = scale;
   s->dropout = dropout_p > 0.f;
-  const double t = std::floor((double)dropout_p * 4294967296.0);
+  const double t = std::floor((double)dropout_p * 65536.0);
   s->drop_thresh = s->dropout ? (uint32_t)t : 0u;
   s->drop_rescale = s->dropout ? 1.0f / (1.0f - dropout_p) : 1.0f;
   s->seed = seed;
@@ -191,7 +191,7 @@ int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_
   if (!keep) return FA_ERR_NULL_POINTER;
   if (b < 0 || h < 0 || N < 1 || (int64_t)N * N > ((int64_t)1 << 40)) return FA_ERR_BAD_SHAPE;
   if (!(dropout_p >= 0.f) || !(dropout_p < 1.f)) return FA_ERR_BAD_ARGUMENT;
-  const uint32_t t = (uint32_t)std::floor((double)dropout_p * 4294967296.0);
+  const uint32_t t = (uint32_t)std::floor((double)dropout_p * 65536.0);
   const hipError_t e = fa::launch_dropout_mask(keep, b, h, N, t, seed, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

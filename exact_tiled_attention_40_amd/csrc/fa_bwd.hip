@@ -267,12 +267,15 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
 
       // ---- P and dS; register r: key j0 + kt*32 + 8*(r/4) + 4*h2 + r%4
       uint32_t spk[8];
+      // dropout: this lane's keep words of the four 8-key groups of the half
+      uint32_t kw[2][2][2];  // [group pair][group of the pair][word]
+      if constexpr (DROPOUT) {
+        keep_words_pair(qi, j0 + kt * 32, h2, h, b, a.seed_lo, a.seed_hi, kw[0]);
+        keep_words_pair(qi, j0 + kt * 32 + 16, h2, h, b, a.seed_lo, a.seed_hi, kw[1]);
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
-        Philox4 rnd;
-        if constexpr (DROPOUT)
-          rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
         float ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -280,10 +283,7 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, -lse2));
           if (kMask && ((CAUSAL && kj4 + e > qi) || kj4 + e >= L)) p = 0.f;
           float dp = pacc[r];
-          if constexpr (DROPOUT) {
-            const uint32_t word = e == 0 ? rnd.x : e == 1 ? rnd.y : e == 2 ? rnd.z : rnd.w;
-            dp *= word >= a.drop_thresh ? a.drop_rescale : 0.f;
-          }
+          if constexpr (DROPOUT) dp *= keep16(kw[g >> 1][g & 1][e >> 1], e & 1, a.drop_thresh) ? a.drop_rescale : 0.f;
           ds[e] = p * (dp - delta);
         }
         spk[2 * g] = pack2<BF16>(ds[0], ds[1]);
@@ -419,35 +419,51 @@ struct HalfCtx {
   uint32_t kb;  // dropout: bit r set if element r is kept
 };
 
-// Dropout keep bits of this lane's key kj against queries q0 .. q0+3 (bit
-// e: query q0 + e kept).  The four lanes of a quad hold keys 4*(kj/4) ..
-// 4*(kj/4)+3 (lane mod 4 = kj mod 4), whose words for one query come from one
-// Philox block (counter (q, kj/4, h, b)): lane c hashes query q0 + c only, and
-// the quad trades the sixteen comparisons, so each block is computed once.
-__device__ __forceinline__ uint32_t dkdv_keep4(const BwdArgs& a, int b, int h, int q0, int kj) {
-  const int c = kj & 3;
-  const Philox4 r = philox4x32_10((uint32_t)(q0 + c), (uint32_t)kj >> 2, (uint32_t)h, (uint32_t)b, a.seed_lo,
-                                  a.seed_hi);
-  const uint32_t t = a.drop_thresh;
-  uint32_t m = (r.x >= t ? 1u : 0u) | (r.y >= t ? 2u : 0u) | (r.z >= t ? 4u : 0u) | (r.w >= t ? 8u : 0u);
-  m <<= 4 * c;                    // bit 4c + k: query q0 + c, key 4*(kj/4) + k
-  m |= quad_perm<1, 0, 3, 2>(m);
-  m |= quad_perm<2, 3, 0, 1>(m);  // all sixteen bits in every lane of the quad
-  m >>= c;                        // bit 4e: query q0 + e, key kj
-  return (m & 1u) | ((m >> 3) & 2u) | ((m >> 6) & 4u) | ((m >> 9) & 8u);
+// Value of lane 8*(l/8) + 7 - l%8 in lane l (DPP half-row mirror; every
+// lane of the octet must be active).
+__device__ __forceinline__ uint32_t octet_mirror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false);
 }
 
 // Keep bits of this lane's key against the 64 queries of the tile at i0:
 // bit 16*qt + r for element r of half qt (query i0 + 32qt + 8*(r/4) +
-// 4*(lane/32) + r%4).  Computed once per tile in a compact loop, so that the
-// unrolled, software-pipelined loop body stays the size of the dropout-free
-// one.
+// 4*(lane/32) + r%4), i.e. bit 4*run + e for query i0 + 8*run + 4*(lane/32) + e.
+// A Philox block (counter (q, kj/8, h, b)) holds the 16-bit values of one
+// query against an aligned group of eight keys, which eight consecutive lanes
+// own (lane mod 8 = kj mod 8).  Round g: lane c of an octet in lane half h2
+// hashes query i0 + 8*(2g + h2) + c, so every block is computed once; the
+// octet gathers its 8 x 8 comparison bits with three DPP steps, the lane
+// halves swap theirs, and each lane keeps the bits of its own key.  Computed
+// once per tile in a compact loop, so that the unrolled, software-pipelined
+// loop body stays the size of the dropout-free one.
 __device__ __forceinline__ uint32_t dkdv_tile_keep(const BwdArgs& a, int b, int h, int i0, int h2, int kj) {
+  const int c = kj & 7;
+  const uint32_t t = a.drop_thresh;
   uint32_t bits = 0;
 #pragma unroll 1
-  for (int g = 0; g < 8; ++g) {
-    const int q0 = i0 + 32 * (g >> 2) + 8 * (g & 3) + 4 * h2;
-    bits |= dkdv_keep4(a, b, h, q0, kj) << (4 * g);
+  for (int g = 0; g < 4; ++g) {
+    const Philox4 r = philox4x32_10((uint32_t)(i0 + 8 * (2 * g + h2) + c), (uint32_t)kj >> 3, (uint32_t)h,
+                                    (uint32_t)b, a.seed_lo, a.seed_hi);
+    // bit 8k + c of lo (keys 0..3 of the group) and of hi (keys 4..7, k - 4):
+    // query c of the run kept against key k
+    uint32_t lo = (keep16(r.x, 0, t) ? 1u : 0u) | (keep16(r.x, 1, t) ? 0x100u : 0u) |
+                  (keep16(r.y, 0, t) ? 0x10000u : 0u) | (keep16(r.y, 1, t) ? 0x1000000u : 0u);
+    uint32_t hi = (keep16(r.z, 0, t) ? 1u : 0u) | (keep16(r.z, 1, t) ? 0x100u : 0u) |
+                  (keep16(r.w, 0, t) ? 0x10000u : 0u) | (keep16(r.w, 1, t) ? 0x1000000u : 0u);
+    lo <<= c;
+    hi <<= c;
+    lo |= quad_perm<1, 0, 3, 2>(lo);
+    hi |= quad_perm<1, 0, 3, 2>(hi);
+    lo |= quad_perm<2, 3, 0, 1>(lo);
+    hi |= quad_perm<2, 3, 0, 1>(hi);
+    lo |= octet_mirror(lo);
+    hi |= octet_mirror(hi);  // the octet's 64 bits in every lane of it
+    // bit q: query q of this half's run (2g + h2) kept against this lane's key
+    uint32_t mine = ((c < 4 ? lo : hi) >> (8 * (c & 3))) & 0xFFu;
+    uint32_t other = mine;
+    permlane32_swap(mine, other);  // mine: run 2g (lanes 0-31), other: run 2g + 1 (lanes 32-63)
+    const uint32_t sh = 4 * h2;
+    bits |= (((mine >> sh) & 0xFu) | (((other >> sh) & 0xFu) << 4)) << (8 * g);
   }
   return bits;
 }

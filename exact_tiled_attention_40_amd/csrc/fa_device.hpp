@@ -37,6 +37,19 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// D += A * B on a 16x16 tile with a K slice of 32.  Lane l holds A row
+// l%16, B column l%16 and one group of eight K elements (group l/16); the
+// accumulator register r of lane l is element (row 4*(l/16) + r, column l%16).
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // Two fp32 values -> two 16-bit floats (round to nearest even) in one word.
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -338,6 +351,35 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     k1 += 0xBB67AE85u;
   }
   return {c0, c1, c2, c3};
+}
+
+// Dropout keep decision of one element from its 16-bit Philox value: the
+// low (hi = 0) or high (hi = 1) half of word w, kept iff >= thresh.
+__device__ __forceinline__ bool keep16(uint32_t w, int hi, uint32_t thresh) {
+  return (hi ? w >> 16 : w & 0xFFFFu) >= thresh;
+}
+
+// Keep words of one query against two aligned 8-key groups, for layouts in
+// which lane half h2 holds keys 4*h2 .. 4*h2+3 of every group (lanes l and
+// l^32 own the same query qi).  The block with counter (qi, group, h, b)
+// holds the 16-bit values of the group's eight keys (value v: half v%2 of
+// word v/2), so a lane half needs two of its four words.  The two lanes of
+// a query split the work: lane half h2 hashes group j8/8 + h2 (j8: first key
+// of the pair), and one permlane32 swap per word pair trades the halves.  On
+// return kw[u][0..1] are this lane's words of group j8/8 + u.
+__device__ __forceinline__ void keep_words_pair(int qi, int j8, int h2, int h, int b, uint32_t seed_lo,
+                                                uint32_t seed_hi, uint32_t (&kw)[2][2]) {
+  const Philox4 r = philox4x32_10((uint32_t)qi, (uint32_t)(j8 >> 3) + (uint32_t)h2, (uint32_t)h, (uint32_t)b,
+                                  seed_lo, seed_hi);
+  // lanes 0-31 keep x, y of their group (j8/8) and send z, w; lanes 32-63
+  // keep z, w of theirs (j8/8 + 1) and send x, y
+  uint32_t a0 = r.x, b0 = r.z, a1 = r.y, b1 = r.w;
+  permlane32_swap(a0, b0);
+  permlane32_swap(a1, b1);
+  kw[0][0] = a0;
+  kw[0][1] = a1;
+  kw[1][0] = b0;
+  kw[1][1] = b1;
 }
 
 }  // namespace fa

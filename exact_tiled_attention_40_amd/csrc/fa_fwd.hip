@@ -319,14 +319,15 @@ __global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_k
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
-          const Philox4 rnd = philox4x32_10((uint32_t)qi, (uint32_t)kj4 >> 2, (uint32_t)h, (uint32_t)b,
-                                            a.seed_lo, a.seed_hi);
-          if (rnd.x < a.drop_thresh) sacc[kt][4 * g + 0] = 0.f;
-          if (rnd.y < a.drop_thresh) sacc[kt][4 * g + 1] = 0.f;
-          if (rnd.z < a.drop_thresh) sacc[kt][4 * g + 2] = 0.f;
-          if (rnd.w < a.drop_thresh) sacc[kt][4 * g + 3] = 0.f;
+        for (int gp = 0; gp < 2; ++gp) {
+          // key groups 2gp, 2gp+1 of this half: words for keys 4*h2 .. 4*h2+3
+          uint32_t kw[2][2];
+          keep_words_pair(qi, j0 + kt * 32 + 16 * gp, h2, h, b, a.seed_lo, a.seed_hi, kw);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!keep16(kw[u][e >> 1], e & 1, a.drop_thresh)) sacc[kt][4 * (2 * gp + u) + e] = 0.f;
         }
     }
 #pragma unroll
@@ -495,19 +496,20 @@ hipError_t launch_fwd_d(const AttnShape& s, const FwdArgs& args, hipStream_t str
                    : launch_fwd_t<D, BF16, false, false>(args, stream);
 }
 
-// Dropout keep mask of one head, N x N bytes: one thread per 4 consecutive
+// Dropout keep mask of one head, N x N bytes: one thread per 8 consecutive
 // columns of a row (one Philox block).
 __global__ __launch_bounds__(256) void fa_dropout_mask_kernel(uint8_t* keep, int b, int h, int N,
                                                               uint32_t thresh, uint32_t seed_lo,
                                                               uint32_t seed_hi) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int groups = (N + 3) / 4;
+  const int groups = (N + 7) / 8;
   if (t >= (int64_t)N * groups) return;
   const int i = (int)(t / groups);
-  const int j4 = (int)(t % groups) * 4;
-  const Philox4 r = philox4x32_10((uint32_t)i, (uint32_t)j4 >> 2, (uint32_t)h, (uint32_t)b, seed_lo, seed_hi);
+  const int j8 = (int)(t % groups) * 8;
+  const Philox4 r = philox4x32_10((uint32_t)i, (uint32_t)j8 >> 3, (uint32_t)h, (uint32_t)b, seed_lo, seed_hi);
   const uint32_t words[4] = {r.x, r.y, r.z, r.w};
-  for (int e = 0; e < 4 && j4 + e < N; ++e) keep[(int64_t)i * N + j4 + e] = words[e] >= thresh ? 1 : 0;
+  for (int e = 0; e < 8 && j8 + e < N; ++e)
+    keep[(int64_t)i * N + j8 + e] = keep16(words[e >> 1], e & 1, thresh) ? 1 : 0;
 }
 
 }  // namespace
@@ -548,7 +550,7 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
 
 hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,
                                hipStream_t stream) {
-  const int64_t work = (int64_t)N * ((N + 3) / 4);
+  const int64_t work = (int64_t)N * ((N + 7) / 8);
   const int64_t nblocks = (work + 255) / 256;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fa_dropout_mask_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, keep, b, h, N,

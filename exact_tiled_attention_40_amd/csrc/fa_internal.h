@@ -15,7 +15,7 @@ struct AttnShape {
   bool bf16;
   float scale;
   bool dropout;
-  uint32_t drop_thresh;    // floor(p * 2^32)
+  uint32_t drop_thresh;    // floor(p * 2^16)
   float drop_rescale;      // 1 / (1 - p)
   uint64_t seed;
   const uint8_t* bmask;    // block mask [B, H, nb, nb] (device) or nullptr: dense

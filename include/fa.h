@@ -41,11 +41,14 @@
  *   - scale multiplies Q K^T before the softmax (1/sqrt(d) is the usual value).
  *   - Dropout (0 < dropout_p < 1) drops entries of the normalised P before
  *     the P V product and scales kept entries by 1/(1 - dropout_p); the
- *     log-sum-exp excludes dropout.  Element (b, h, i, j) is kept iff word
- *     j mod 4 of Philox-4x32-10 with key (seed low 32 bits, seed high 32
- *     bits) and counter (i, j / 4, h, b) is >= floor(dropout_p * 2^32)
- *     (Salmon et al., SC'11).  Forward and backward must get the same seed and
- *     dropout_p.  dropout_p == 0 runs the no-dropout kernels.
+ *     log-sum-exp excludes dropout.  Philox-4x32-10 (Salmon et al., SC'11)
+ *     with key (seed low 32 bits, seed high 32 bits) and counter
+ *     (i, j / 8, h, b) gives four 32-bit words, read as eight 16-bit values
+ *     (value v: low half of word v/2 for even v, high half for odd v);
+ *     element (b, h, i, j) is kept iff value j mod 8 is
+ *     >= floor(dropout_p * 2^16), so the drop probability is that threshold
+ *     / 2^16 (within 2^-16 of dropout_p).  Forward and backward must get the
+ *     same seed and dropout_p.  dropout_p == 0 runs the no-dropout kernels.
  *   - dtype is FA_DTYPE_F16 or FA_DTYPE_BF16 for every tensor except lse and
  *     the workspace (float32).  d must be 32, 64, 96 or 128: head sizes up to
  *     128 are the fused-kernel range in the tiemojia.cn article's list of

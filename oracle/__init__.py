@@ -91,9 +91,9 @@ def _iptr(a):
 
 
 def dropout_threshold(p: float) -> int:
-    """floor(p * 2^32) for the float32 value of p (an element is kept iff its
-    Philox word is >= this threshold)."""
-    return int(math.floor(float(np.float32(p)) * 4294967296.0))
+    """floor(p * 2^16) for the float32 value of p (an element is kept iff its
+    16-bit Philox value is >= this threshold)."""
+    return int(math.floor(float(np.float32(p)) * 65536.0))
 
 
 def _seq_layout(tokens: int, N: int | None, lengths):

@@ -45,9 +45,11 @@
  * Dropout keep bits come from Philox-4x32-10 (Salmon, Moraes, Dror, Shaw,
  * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11), written here from
  * that paper: key = (seed low word, seed high word); counter =
- * (row i, col j / 4, head h, batch-or-sequence b); column j uses output word
- * j mod 4; the element is kept iff that word >= thresh, where the caller
- * passes thresh = floor(p * 2^32).  Row and column indices are local to the
+ * (row i, col j / 8, head h, batch-or-sequence b).  The four 32-bit output
+ * words are read as eight 16-bit values, value v = low half of word v/2 for
+ * even v and high half for odd v; column j uses value j mod 8, and the
+ * element is kept iff that value >= thresh, where the caller passes
+ * thresh = floor(p * 2^16).  Row and column indices are local to the
  * sequence.
  */
 #include <math.h>
@@ -90,11 +92,12 @@ void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
 
 int oracle_keep(uint64_t seed, uint32_t thresh, int b, int h, int i, int j)
 {
-    uint32_t ctr[4] = {(uint32_t)i, (uint32_t)j >> 2, (uint32_t)h, (uint32_t)b};
+    uint32_t ctr[4] = {(uint32_t)i, (uint32_t)j >> 3, (uint32_t)h, (uint32_t)b};
     uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     uint32_t out[4];
     oracle_philox4x32_10(ctr, key, out);
-    return out[j & 3] >= thresh;
+    uint32_t v = (j & 1) ? out[(j & 7) >> 1] >> 16 : out[(j & 7) >> 1] & 0xFFFFu;
+    return v >= thresh;
 }
 
 /* Keep mask of one (b, h) head, row-major L x L bytes (1 = kept). */
@@ -112,7 +115,7 @@ typedef struct {
     int causal;
     int dropout;      /* 0: no dropout */
     double keep_scale;/* 1/(1-p) */
-    uint32_t thresh;  /* floor(p * 2^32) */
+    uint32_t thresh;  /* floor(p * 2^16) */
     uint64_t seed;
     int b, h;         /* counter indices of this head */
     const uint8_t* bmask; /* NULL, or [nbq][nbk] block mask of this head */

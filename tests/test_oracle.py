@@ -301,25 +301,35 @@ def test_keep_mask_uses_documented_counter_layout():
     seed, p = 0x123456789ABCDEF0, 0.25
     t = oracle.dropout_threshold(p)
     m = oracle.keep_mask(seed, p, b=3, h=5, L=13)
+    assert t == int(0.25 * 65536)
     for i in range(13):
         for j in range(13):
-            words = oracle.philox4x32_10([i, j // 4, 5, 3], [seed & 0xFFFFFFFF, seed >> 32])
-            assert m[i, j] == (words[j % 4] >= t)
+            words = oracle.philox4x32_10([i, j // 8, 5, 3], [seed & 0xFFFFFFFF, seed >> 32])
+            value = (words[(j % 8) // 2] >> (16 * (j % 2))) & 0xFFFF
+            assert m[i, j] == (value >= t)
 
 
 def test_keep_threshold_boundary():
-    # an element whose Philox word equals the threshold is kept; one above is dropped
-    seed, b, h, i, j = 42, 1, 2, 3, 6
-    w = oracle.philox4x32_10([i, j // 4, h, b], [seed, 0])[j % 4]
-    assert oracle.keep(seed, w, b, h, i, j)
-    assert not oracle.keep(seed, w + 1, b, h, i, j)
+    # an element whose 16-bit Philox value equals the threshold is kept; one
+    # above is dropped (both halves of a word: columns 6 and 7 share word 3)
+    seed, b, h, i = 42, 1, 2, 3
+    words = oracle.philox4x32_10([i, 0, h, b], [seed, 0])
+    for j, v in ((6, words[3] & 0xFFFF), (7, words[3] >> 16)):
+        assert oracle.keep(seed, v, b, h, i, j)
+        assert not oracle.keep(seed, v + 1, b, h, i, j)
+
+
+def test_dropout_threshold_values():
+    assert oracle.dropout_threshold(0.1) == 6553           # floor(0.1f * 65536)
+    assert oracle.dropout_threshold(0.5) == 32768
+    assert oracle.dropout_threshold(0.999) == 65470
 
 
 def test_keep_rate_statistics():
     p = 0.1
     m = oracle.keep_mask(1005, p, b=0, h=0, L=700)
     n = m.size
-    expect = 1.0 - oracle.dropout_threshold(p) / 2**32
+    expect = 1.0 - oracle.dropout_threshold(p) / 2**16
     sigma = math.sqrt(n * expect * (1 - expect))
     assert abs(int(m.sum()) - n * expect) < 5 * sigma
     # different heads / batches give different masks
