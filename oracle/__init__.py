@@ -48,6 +48,9 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int)
         u32p = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_rows_head.argtypes = [dp, dp, dp, dp, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_double, ctypes.c_int, ctypes.c_int, ip, dp, dp, dp]
+        lib.oracle_rows_head.restype = None
         lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
         lib.oracle_philox4x32_10.restype = None
         lib.oracle_keep.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
@@ -210,6 +213,35 @@ def decode(q, k_cache, v_cache, *, scale: float, causal: bool, seqlens_k=None):
     lib.oracle_decode(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse), B, H, nq, nk, d, _iptr(lk),
                       float(scale), int(bool(causal)))
     return o, lse
+
+
+def rows_head(q, k, v, dout=None, *, scale: float, causal: bool, rows):
+    """O, LSE (and dQ if dout is given) of the listed query rows of one head,
+    without forming P: q, k, v, dout float64 [L, d] (any row stride).
+    Returns o [n, d], lse [n], dq [n, d] or None.  No dropout, no mask."""
+    lib = _load()
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L, d = q.shape
+    ld = q.strides[0] // 8
+    for t in (k, v) + ((dout,) if dout is not None else ()):
+        t = np.asarray(t)
+        if t.shape != (L, d) or t.strides != q.strides or t.dtype != np.float64:
+            raise ValueError("q, k, v, dout must share shape and strides")
+    if q.strides[1] != 8:
+        raise ValueError("rows must be contiguous in the head dimension")
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    if rows.size and (rows.min() < 0 or rows.max() >= L):
+        raise ValueError("row out of range")
+    n = rows.size
+    o = np.zeros((n, d))
+    lse = np.zeros(n)
+    dq = np.zeros((n, d)) if dout is not None else None
+    dptr = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_rows_head(q.ctypes.data_as(dptr), k.ctypes.data_as(dptr), v.ctypes.data_as(dptr),
+                         dout.ctypes.data_as(dptr) if dout is not None else None, ld, L, d, float(scale),
+                         int(bool(causal)), n, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), _dptr(o),
+                         _dptr(lse), _dptr(dq) if dq is not None else None)
+    return o, lse, dq
 
 
 def philox4x32_10(counter, key):

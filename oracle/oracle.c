@@ -455,6 +455,51 @@ void oracle_decode(const double* q, const double* k, const double* v, double* o,
         }
 }
 
+/* Selected query rows of one head, for sequences too long to hold P:
+ * for each listed row i, the definition restricted to that row (no dropout,
+ * no block mask) -- s_j = scale q_i.k_j over the visible keys j, m = max s,
+ * p_j = e^{s_j - m} / sum_j e^{s_j - m}, o_i = sum_j p_j v_j and
+ * LSE_i = m + ln sum_j e^{s_j - m} (lab write-up, section 2.1); and, when
+ * dout is given, the same analytic backward as oracle_bwd_head restricted
+ * to row i: D_i = dO_i.o_i, dp_j = dO_i.v_j, dS_j = p_j (dp_j - D_i),
+ * dQ_i = scale sum_j dS_j k_j.  q, k, v, dout hold rows of one head with
+ * ld elements between tokens; o, dq are [nrows][d], lse [nrows]. */
+void oracle_rows_head(const double* q, const double* k, const double* v, const double* dout, long ld, int L,
+                      int d, double scale, int causal, int nrows, const int* rows, double* o, double* lse,
+                      double* dq)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        const int i = rows[r];
+        const int nv = causal ? i + 1 : L;
+        double* p = (double*)malloc(sizeof(double) * (size_t)nv);
+        double m = -INFINITY;
+        for (int j = 0; j < nv; ++j) {
+            p[j] = scale * dot(q + (size_t)i * ld, k + (size_t)j * ld, d);
+            if (p[j] > m) m = p[j];
+        }
+        double sum = 0.0;
+        for (int j = 0; j < nv; ++j) sum += exp(p[j] - m);
+        for (int j = 0; j < nv; ++j) p[j] = exp(p[j] - m) / sum;
+        lse[r] = m + log(sum);
+        double* oi = o + (size_t)r * d;
+        for (int c = 0; c < d; ++c) oi[c] = 0.0;
+        for (int j = 0; j < nv; ++j)
+            for (int c = 0; c < d; ++c) oi[c] += p[j] * v[(size_t)j * ld + c];
+        if (dout) {
+            const double* g = dout + (size_t)i * ld;
+            const double D = dot(g, oi, d);
+            double* dqi = dq + (size_t)r * d;
+            for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+            for (int j = 0; j < nv; ++j) {
+                const double ds = p[j] * (dot(g, v + (size_t)j * ld, d) - D);
+                for (int c = 0; c < d; ++c) dqi[c] += scale * ds * k[(size_t)j * ld + c];
+            }
+        }
+        free(p);
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -554,3 +554,22 @@ def test_decode_queries_that_see_no_key():
     assert np.all(o[0, :2] == 0.0) and np.all(np.isneginf(lse[0, :2]))
     np.testing.assert_allclose(o[0, 2, 0], vc[0, 0, 0], atol=1e-15)
     assert np.isclose(lse[0, 2, 0], 0.5 * float(q[0, 2, 0] @ kc[0, 0, 0]), atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_head_equals_full_head(causal):
+    # the row-subset oracle (for sequences too long to form P) gives the same
+    # O, LSE and dQ rows as the full-head definition, on a strided head view
+    L, H, d, s = 41, 3, 8, 0.37
+    q, k, v, do = (rnd((L, H, d), 700 + i) for i in range(4))
+    o, lse = oracle.forward(q, k, v, scale=s, causal=causal, N=L)
+    dq, _, _ = oracle.backward(q, k, v, do, scale=s, causal=causal, N=L)
+    rows = [0, 1, 5, 17, 39, 40]
+    for h in range(H):
+        ro, rl, rdq = oracle.rows_head(q[:, h], k[:, h], v[:, h], do[:, h], scale=s, causal=causal, rows=rows)
+        np.testing.assert_allclose(ro, o[rows, h], atol=1e-13)
+        np.testing.assert_allclose(rl, lse[rows, h], atol=1e-13)
+        np.testing.assert_allclose(rdq, dq[rows, h], atol=1e-13)
+    ro, rl, none = oracle.rows_head(q[:, 0], k[:, 0], v[:, 0], scale=s, causal=causal, rows=rows)
+    assert none is None
+    np.testing.assert_allclose(ro, o[rows, 0], atol=1e-13)
