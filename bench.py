@@ -25,6 +25,7 @@ MFMA, 2.5 PFLOP/s.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -261,6 +262,8 @@ def main() -> int:
                          "(diagonal blocks kept); 0 = dense")
     ap.add_argument("--decode", action="store_true",
                     help="time fa_decode (KV-cache decode step) on a decode workload instead")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="run the chosen workload with this head size instead (32, 64, 96 or 128)")
     ap.add_argument("--settle-s", type=float, default=1.5,
                     help="repeat the warm-up steps until this many seconds have passed (clock settling)")
     args = ap.parse_args()
@@ -282,6 +285,9 @@ def main() -> int:
     import workloads
 
     wl = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+    if args.head_dim and args.head_dim != wl.d:
+        # same recipe and seed at another head size (the head-size sweep)
+        wl = dataclasses.replace(wl, name=wl.name.replace(f"_d{wl.d}_", f"_d{args.head_dim}_"), d=args.head_dim)
     x = workloads.make_inputs(wl)
     dev = torch.device("cuda")
     if x.qkv is not None:
