@@ -3,8 +3,9 @@
 // "FlashAttention" (dpshk.com), section 3.3).  Two kernels on one stream;
 // neither uses atomics:
 //
-//   fa_bwd_dq_kernel    one workgroup per (b, h, block of 128 queries), four
-//                       waves of 32 queries.  Prologue: D = rowsum(dO * O)
+//   fa_bwd_dq_kernel    one workgroup per (b, h, block of 256 queries), eight
+//                       waves of 32 queries (block-sparse: 128 queries, four
+//                       waves, one mask row).  Prologue: D = rowsum(dO * O)
 //                       for its rows (kept in registers and written to the
 //                       workspace).  For every 64-key tile the queries can
 //                       see (K and V tiles double-buffered HBM -> LDS):
@@ -43,9 +44,11 @@ namespace {
 
 constexpr int kWaves = 4;          // dK/dV kernel: one wave per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWavesQ = 4;         // dQ kernel: two workgroups (waves) per SIMD
-constexpr int kThreadsQ = 64 * kWavesQ;
-constexpr int kBQ = 32 * kWavesQ;  // queries per dQ workgroup
+// dQ kernel: dense, eight waves (two per SIMD, one workgroup per CU), so
+// each K/V tile in LDS serves 256 queries; block-sparse, four waves (128
+// queries, one mask row, so the tile list is exact) and two workgroups per CU.
+template <bool SPARSE> constexpr int dq_waves() { return SPARSE ? 4 : 8; }
+template <bool SPARSE> constexpr int dq_rows() { return 32 * dq_waves<SPARSE>(); }
 constexpr int kBC = 64;            // keys per tile of the dQ kernel
 constexpr int kBKV = 32 * kWaves;  // keys per dK/dV workgroup
 constexpr int kBR = 64;            // queries per tile of the dK/dV kernel
@@ -89,8 +92,10 @@ __device__ __forceinline__ void seq_range(const BwdArgs& a, int b, int& start, i
 
 // ---------------------------------------------------------------- dQ (+ D)
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
-__global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * dq_waves<SPARSE>(), SPARSE ? 2 : 1) void fa_bwd_dq_kernel(BwdArgs a) {
   using T = MTile<D, kBC>;
+  constexpr int kWavesQ = dq_waves<SPARSE>();
+  constexpr int kBQ = dq_rows<SPARSE>();
   constexpr int kNS = 2 * (D / 16);  // S^T and dP^T products per 32-key half (D/16 k-steps each)
   constexpr int kNQ = 2 * (D / 32);  // dQ^T products per 32-key half (two 16-key slices x D/32 tiles)
   constexpr int kPF = 2;             // LDS operand reads in flight (products ahead)
@@ -183,11 +188,14 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
     const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
-    static_assert(T::kBlocks % kWavesQ == 0, "tile blocks must split evenly over the waves");
+    // wave w loads blocks w, w + kWavesQ, ... (a partial last round when
+    // the tile has fewer blocks than a multiple of the waves)
 #pragma unroll
-    for (int u = 0; u < T::kBlocks / kWavesQ; ++u) {
-      T::load(kr, ks0 + buf * T::kBytes, row_bytes, u * kWavesQ + w, lane);
-      T::load(vr, vs0 + buf * T::kBytes, row_bytes, u * kWavesQ + w, lane);
+    for (int u = 0; u < (T::kBlocks + kWavesQ - 1) / kWavesQ; ++u) {
+      if (u * kWavesQ + w < T::kBlocks) {
+        T::load(kr, ks0 + buf * T::kBytes, row_bytes, u * kWavesQ + w, lane);
+        T::load(vr, vs0 + buf * T::kBytes, row_bytes, u * kWavesQ + w, lane);
+      }
     }
   };
 
@@ -204,6 +212,7 @@ __global__ __launch_bounds__(kThreadsQ, 2) void fa_bwd_dq_kernel(BwdArgs a) {
   int n_list = ntiles;
   if constexpr (SPARSE) {
     if (w == 0) {
+      static_assert(!SPARSE || kBQ == kMaskBlock, "one mask row per block-sparse workgroup");
       const uint8_t* mrow = a.bmask + (((int64_t)b * a.H + h) * a.nb + q0 / kMaskBlock) * a.nb;
       const int n = build_tile_list(mrow, nullptr, 0, 1, ntiles, tlist, tflag, lane);
       if (lane == 0) tcount[0] = n;
@@ -940,8 +949,8 @@ hipError_t launch_bwd_s(const AttnShape& s, const BwdArgs& args, int stages, hip
   if (stages & kBwdDq) {
     const int64_t nb = (int64_t)args.nqb * s.B * s.H;
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb), dim3(kThreadsQ),
-                       0, stream, args);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb),
+                       dim3(64 * dq_waves<SPARSE>()), 0, stream, args);
   }
   if (stages & kBwdKV) {
     const int64_t nb = (int64_t)args.nkb * s.B * s.H;
@@ -989,7 +998,8 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
   a.B = s.B;
   a.H = s.H;
   a.N = s.N;
-  a.nqb = (s.N + kBQ - 1) / kBQ;
+  const int bq = s.bmask ? dq_rows<true>() : dq_rows<false>();
+  a.nqb = (s.N + bq - 1) / bq;
   a.nkb = (s.N + kBKV - 1) / kBKV;
   a.scale = s.scale;
   a.scale_log2 = s.scale * kLog2e;
