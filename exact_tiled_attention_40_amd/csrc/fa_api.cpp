@@ -26,7 +26,9 @@ int check_common(int B, int H, int N, int d, float scale, float dropout_p, int d
   const int64_t hd = (int64_t)H * d;
   const int64_t ld = ld_qkv == 0 ? hd : ld_qkv;
   if (ld < hd || (ld % 8) != 0) return FA_ERR_ALIGNMENT;
-  if (cu_seqlens && !aligned16(cu_seqlens) && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return FA_ERR_ALIGNMENT;
+  // the kernels address a 64-token tile through a 32-bit buffer range
+  if (ld > FA_MAX_TOKEN_STRIDE) return FA_ERR_UNSUPPORTED;
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return FA_ERR_ALIGNMENT;
   s->B = B;
   s->H = H;
   s->N = N;

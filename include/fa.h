@@ -54,7 +54,10 @@
  *     128 are the fused-kernel range in the tiemojia.cn article's list of
  *     when the fused kernel applies (its engineering-considerations part);
  *     the lab write-up, section 5.3, warns that kernels degrade past 192.
- *   - Pointers must be 16-byte aligned and ld_qkv a multiple of 8.
+ *   - Pointers must be 16-byte aligned and ld_qkv a multiple of 8; the
+ *     token stride (ld_qkv, or H*d) may not exceed FA_MAX_TOKEN_STRIDE
+ *     elements (FA_ERR_UNSUPPORTED otherwise: the kernels address a tile of
+ *     64 tokens through a 32-bit byte range).
  *   - Outputs must not alias inputs; dq, dk and dv may point into one packed
  *     [B, N, 3, H, d] buffer when ld_qkv = 3*H*d.
  *   - Every argument is checked on the host before any HIP call; a failed
@@ -70,6 +73,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Largest token stride (elements between consecutive tokens) of q, k, v,
+ * dq, dk, dv, o and dout that fa_forward / fa_backward accept. */
+#define FA_MAX_TOKEN_STRIDE (1 << 24)
 
 enum fa_dtype { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 };
 

@@ -82,6 +82,7 @@ def fwd(lib, **over):
     (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=0.0), 4), (dict(scale=-1.0), 4),
     (dict(p=1.0), 4), (dict(p=-0.1), 4), (dict(p=float("nan")), 4),
     (dict(ld=100), 5), (dict(ld=127), 5), (dict(q=P + 8), 5), (dict(o=P + 2), 5), (dict(lse=P + 4), 5),
+    (dict(ld=(1 << 24) + 8), 3), (dict(H=(1 << 18) + 1, d=64), 3),
 ])
 def test_forward_rejects_bad_arguments(lib, over, code):
     assert fwd(lib, **over) == code
