@@ -573,3 +573,25 @@ def test_rows_head_equals_full_head(causal):
     ro, rl, none = oracle.rows_head(q[:, 0], k[:, 0], v[:, 0], scale=s, causal=causal, rows=rows)
     assert none is None
     np.testing.assert_allclose(ro, o[rows, 0], atol=1e-13)
+
+
+@pytest.mark.parametrize("openmp", [False, True])
+def test_oracle_runs_clean_under_sanitizers(tmp_path, openmp):
+    # every oracle entry point on exactly sized heap buffers (empty sequences,
+    # block masks, dropout, head selection, decode with an empty cache, row
+    # subsets) under AddressSanitizer + UndefinedBehaviorSanitizer, serial and
+    # with OpenMP threads
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "oracle_sanitize")
+    cmd = [gcc, "-std=c11", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", os.path.join(os.path.dirname(HERE), "oracle", "oracle.c"),
+           os.path.join(HERE, "helpers", "oracle_sanitize.c"), "-lm", "-o", exe]
+    if openmp:
+        cmd.insert(1, "-fopenmp")
+    subprocess.check_call(cmd)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", OMP_NUM_THREADS="4")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "clean" in r.stdout
