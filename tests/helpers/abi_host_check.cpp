@@ -1,0 +1,109 @@
+// Host-only check of the C-ABI front end (fa_api.cpp), built with
+// AddressSanitizer + UndefinedBehaviorSanitizer against recording stubs of
+// the kernel launchers (no GPU, no HIP runtime calls): every entry point is
+// driven through its error paths and its accepted paths, and the launch
+// description that reaches the launchers is checked (dropout threshold and
+// scale, token stride, mask blocks, workspace carving, backward stages).
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "fa.h"
+#include "../../exact_tiled_attention_40_amd/csrc/fa_internal.h"
+
+namespace {
+int calls = 0;
+fa::AttnShape last{};
+int last_stages = 0;
+const float *last_delta = nullptr, *last_lse2 = nullptr;
+uint32_t last_thresh = 0;
+}  // namespace
+
+namespace fa {
+hipError_t launch_forward(const AttnShape& s, const void*, const void*, const void*, void*, float*, hipStream_t) {
+  ++calls;
+  last = s;
+  return hipSuccess;
+}
+hipError_t launch_backward(const AttnShape& s, const void*, const void*, const void*, const void*, const float*,
+                           const void*, void*, void*, void*, float* delta, float* lse2, int stages, hipStream_t) {
+  ++calls;
+  last = s;
+  last_stages = stages;
+  last_delta = delta;
+  last_lse2 = lse2;
+  return hipSuccess;
+}
+int decode_splits(int nk) { return (nk + 1023) / 1024; }
+hipError_t launch_decode(const DecodeShape&, const void*, const void*, const void*, const int32_t*, void*, float*,
+                         float*, hipStream_t) {
+  ++calls;
+  return hipSuccess;
+}
+hipError_t launch_dropout_mask(uint8_t*, int, int, int, uint32_t thresh, uint64_t, hipStream_t) {
+  ++calls;
+  last_thresh = thresh;
+  return hipSuccess;
+}
+}  // namespace fa
+
+#define CHECK(cond)                                                   \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      std::fprintf(stderr, "check failed line %d: %s\n", __LINE__, #cond); \
+      return 1;                                                       \
+    }                                                                 \
+  } while (0)
+
+int main() {
+  // fake, aligned addresses: the stubs never dereference them
+  void* P = reinterpret_cast<void*>(static_cast<uintptr_t>(0x10000));
+  float* F = static_cast<float*>(P);
+  const int32_t* CU = static_cast<const int32_t*>(P);
+  // forward: accepted, with the launch description checked
+  CHECK(fa_forward(P, P, P, P, F, 2, 3, 100, 64, 0.125f, 1, nullptr, 0.1f, 7, nullptr, FA_DTYPE_BF16, 0) == FA_OK);
+  CHECK(calls == 1 && last.B == 2 && last.H == 3 && last.N == 100 && last.d == 64 && last.ld == 3 * 64);
+  CHECK(last.causal && last.bf16 && last.dropout && last.drop_thresh == 6553u && last.bmask == nullptr);
+  CHECK(std::fabs(last.drop_rescale - 1.0f / 0.9f) < 1e-6f && last.seed == 7);
+  CHECK(fa_forward(P, P, P, P, F, 1, 2, 5, 128, 1.f, 0, CU, 0.f, 0, nullptr, FA_DTYPE_F16, 3 * 2 * 128) == FA_OK);
+  CHECK(!last.dropout && last.drop_thresh == 0 && last.ld == 768 && last.cu == CU && !last.bf16);
+  // forward: rejected before any launch
+  const int before = calls;
+  CHECK(fa_forward(nullptr, P, P, P, F, 1, 1, 8, 64, 1.f, 0, nullptr, 0.f, 0, nullptr, 1, 0) == FA_ERR_NULL_POINTER);
+  CHECK(fa_forward(P, P, P, P, F, 0, 1, 8, 64, 1.f, 0, nullptr, 0.f, 0, nullptr, 1, 0) == FA_ERR_BAD_SHAPE);
+  CHECK(fa_forward(P, P, P, P, F, 1, 1, 8, 80, 1.f, 0, nullptr, 0.f, 0, nullptr, 1, 0) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward(P, P, P, P, F, 1, 1, 8, 64, NAN, 0, nullptr, 0.f, 0, nullptr, 1, 0) == FA_ERR_BAD_ARGUMENT);
+  CHECK(fa_forward(P, P, P, P, F, 1, 1, 8, 64, 1.f, 0, nullptr, 1.f, 0, nullptr, 1, 0) == FA_ERR_BAD_ARGUMENT);
+  CHECK(fa_forward(P, P, P, P, F, 1, 1, 8, 64, 1.f, 0, nullptr, 0.f, 0, nullptr, 1, 60) == FA_ERR_ALIGNMENT);
+  CHECK(fa_forward(P, P, P, P, F, 1, 1, 8, 64, 1.f, 0, nullptr, 0.f, 0, nullptr, 1, (1 << 24) + 8) ==
+        FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward(P, P, P, P, F, 70000, 1, 70000, 64, 1.f, 0, nullptr, 0.f, 0, nullptr, 1, 0) == FA_ERR_BAD_SHAPE);
+  CHECK(calls == before);
+  // block-sparse forward: mask blocks
+  CHECK(fa_forward_block_sparse(P, P, P, P, F, 1, 2, 300, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0,
+                                static_cast<const uint8_t*>(P)) == FA_OK);
+  CHECK(last.nb == 3 && last.bmask == P);
+  CHECK(fa_forward_block_sparse(P, P, P, P, F, 1, 2, FA_MASK_MAX_N + 1, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1,
+                                0, static_cast<const uint8_t*>(P)) == FA_ERR_UNSUPPORTED);
+  // backward: workspace carving and stages
+  const size_t need = fa_backward_workspace_size(2, 100, 3, 64);
+  CHECK(need == 2 * ((2 * 100 * 3 * 4 + 255) / 256 * 256));
+  CHECK(fa_backward(P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0, P,
+                    need - 1) == FA_ERR_WORKSPACE);
+  CHECK(fa_backward(P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0, P, need) ==
+        FA_OK);
+  CHECK(last_stages == 3 && last_delta == F && last_lse2 == F + need / 2 / 4);
+  CHECK(fa_backward_stage(1, P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0, P,
+                          need) == FA_OK);
+  CHECK(last_stages == 2);
+  // decode and the dropout-mask export
+  const size_t dneed = fa_decode_workspace_size(2, 4, 1, 3000, 128);
+  CHECK(dneed > 0);
+  CHECK(fa_decode(P, P, P, nullptr, P, F, 2, 4, 1, 3000, 128, 0.1f, 1, nullptr, 1, P, dneed) == FA_OK);
+  CHECK(fa_decode(P, P, P, nullptr, P, F, 2, 4, 5, 3000, 128, 0.1f, 1, nullptr, 1, P, dneed) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_dropout_mask(static_cast<uint8_t*>(P), 0, 0, 16, 0.25f, 1, nullptr) == FA_OK && last_thresh == 16384u);
+  for (int c = 0; c <= 8; ++c) CHECK(fa_strerror(c) != nullptr && std::strlen(fa_strerror(c)) > 0);
+  std::printf("abi host check: clean (%d launches)\n", calls);
+  return 0;
+}

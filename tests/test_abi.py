@@ -7,11 +7,13 @@ never made on the CPU.
 import ctypes
 import os
 import re
+import shutil
 import subprocess
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.dirname(os.path.abspath(__file__))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 LIB = os.path.join(ROOT, "exact_tiled_attention_40_amd", "libfa.so")
 
@@ -200,3 +202,24 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(q=P + 8) == 5 and call(lse=P + 4) == 5 and call(lens=P + 2) == 5
     assert call(ws=None) == 6 and call(wsb=need - 1) == 6
     assert call(ws=P + 4) == 5
+
+
+def test_abi_front_end_under_sanitizers(tmp_path):
+    # fa_api.cpp built for the host with AddressSanitizer + UBSan against
+    # recording stubs of the kernel launchers: every entry point's error and
+    # accepted paths, and the launch description the launchers receive
+    # (dropout threshold and scale, token stride, mask blocks, workspace
+    # carving, backward stages).  No GPU, no HIP runtime call.
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "abi_host_check")
+    host_sanitizers = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+    subprocess.check_call([hipcc, "-x", "hip", "--offload-arch=gfx950", "-O1", "-g", *host_sanitizers,
+                           "-fno-omit-frame-pointer", "-I" + os.path.join(ROOT, "include"),
+                           os.path.join(ROOT, "exact_tiled_attention_40_amd", "csrc", "fa_api.cpp"),
+                           os.path.join(HERE, "helpers", "abi_host_check.cpp"), "-o", exe],
+                          stderr=subprocess.DEVNULL)
+    r = subprocess.run([exe], capture_output=True, text=True, env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0"))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "clean" in r.stdout
