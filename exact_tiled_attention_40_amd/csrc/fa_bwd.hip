@@ -439,42 +439,94 @@ __device__ __forceinline__ uint32_t octet_mirror(uint32_t v) {
 // 4*(lane/32) + r%4), i.e. bit 4*run + e for query i0 + 8*run + 4*(lane/32) + e.
 // A Philox block (counter (q, kj/8, h, b)) holds the 16-bit values of one
 // query against an aligned group of eight keys, which eight consecutive lanes
-// own (lane mod 8 = kj mod 8).  Round g: lane c of an octet in lane half h2
-// hashes query i0 + 8*(2g + h2) + c, so every block is computed once; the
-// octet gathers its 8 x 8 comparison bits with three DPP steps, the lane
-// halves swap theirs, and each lane keeps the bits of its own key.  Computed
-// once per tile in a compact loop, so that the unrolled, software-pipelined
-// loop body stays the size of the dropout-free one.
+// own (lane mod 8 = kj mod 8).  Round g (0..3): lane c of an octet in lane
+// half h2 hashes query i0 + 8*(2g + h2) + c, so every block is computed once;
+// the octet gathers its 8 x 8 comparison bits with three DPP steps, the lane
+// halves swap theirs, and each lane keeps the bits of its own key.
+
+// Philox counter of round g.
+__device__ __forceinline__ void keep_counter(int i0, int g, int h2, int kj, int h, int b, uint32_t (&c)[4]) {
+  c[0] = (uint32_t)(i0 + 8 * (2 * g + h2) + (kj & 7));
+  c[1] = (uint32_t)kj >> 3;
+  c[2] = (uint32_t)h;
+  c[3] = (uint32_t)b;
+}
+
+// Comparisons of a finished block: bit 8k + c of lo (keys 0..3 of the group)
+// and of hi (keys 4..7, k - 4): query c of the run kept against key k.
+__device__ __forceinline__ void keep_compare(const uint32_t (&r)[4], uint32_t t, int c, uint32_t& lo,
+                                             uint32_t& hi) {
+  lo = (keep16(r[0], 0, t) ? 1u : 0u) | (keep16(r[0], 1, t) ? 0x100u : 0u) |
+       (keep16(r[1], 0, t) ? 0x10000u : 0u) | (keep16(r[1], 1, t) ? 0x1000000u : 0u);
+  hi = (keep16(r[2], 0, t) ? 1u : 0u) | (keep16(r[2], 1, t) ? 0x100u : 0u) |
+       (keep16(r[3], 0, t) ? 0x10000u : 0u) | (keep16(r[3], 1, t) ? 0x1000000u : 0u);
+  lo <<= c;
+  hi <<= c;
+}
+
+// The octet's 64 comparison bits in every lane of it.
+__device__ __forceinline__ void keep_gather(uint32_t& lo, uint32_t& hi) {
+  lo |= quad_perm<1, 0, 3, 2>(lo);
+  hi |= quad_perm<1, 0, 3, 2>(hi);
+  lo |= quad_perm<2, 3, 0, 1>(lo);
+  hi |= quad_perm<2, 3, 0, 1>(hi);
+  lo |= octet_mirror(lo);
+  hi |= octet_mirror(hi);
+}
+
+// Tile bits 8g .. 8g+7 from the gathered comparisons of round g.
+__device__ __forceinline__ uint32_t keep_extract(uint32_t lo, uint32_t hi, int c, int h2) {
+  // bit q: query q of this half's run (2g + h2) kept against this lane's key
+  uint32_t mine = ((c < 4 ? lo : hi) >> (8 * (c & 3))) & 0xFFu;
+  uint32_t other = mine;
+  permlane32_swap(mine, other);  // mine: run 2g (lanes 0-31), other: run 2g + 1 (lanes 32-63)
+  const uint32_t sh = 4 * h2;
+  return ((mine >> sh) & 0xFu) | (((other >> sh) & 0xFu) << 4);
+}
+
+// All of a tile's keep bits in one compact loop (the pipeline prologue).
 __device__ __forceinline__ uint32_t dkdv_tile_keep(const BwdArgs& a, int b, int h, int i0, int h2, int kj) {
-  const int c = kj & 7;
-  const uint32_t t = a.drop_thresh;
   uint32_t bits = 0;
 #pragma unroll 1
   for (int g = 0; g < 4; ++g) {
-    const Philox4 r = philox4x32_10((uint32_t)(i0 + 8 * (2 * g + h2) + c), (uint32_t)kj >> 3, (uint32_t)h,
-                                    (uint32_t)b, a.seed_lo, a.seed_hi);
-    // bit 8k + c of lo (keys 0..3 of the group) and of hi (keys 4..7, k - 4):
-    // query c of the run kept against key k
-    uint32_t lo = (keep16(r.x, 0, t) ? 1u : 0u) | (keep16(r.x, 1, t) ? 0x100u : 0u) |
-                  (keep16(r.y, 0, t) ? 0x10000u : 0u) | (keep16(r.y, 1, t) ? 0x1000000u : 0u);
-    uint32_t hi = (keep16(r.z, 0, t) ? 1u : 0u) | (keep16(r.z, 1, t) ? 0x100u : 0u) |
-                  (keep16(r.w, 0, t) ? 0x10000u : 0u) | (keep16(r.w, 1, t) ? 0x1000000u : 0u);
-    lo <<= c;
-    hi <<= c;
-    lo |= quad_perm<1, 0, 3, 2>(lo);
-    hi |= quad_perm<1, 0, 3, 2>(hi);
-    lo |= quad_perm<2, 3, 0, 1>(lo);
-    hi |= quad_perm<2, 3, 0, 1>(hi);
-    lo |= octet_mirror(lo);
-    hi |= octet_mirror(hi);  // the octet's 64 bits in every lane of it
-    // bit q: query q of this half's run (2g + h2) kept against this lane's key
-    uint32_t mine = ((c < 4 ? lo : hi) >> (8 * (c & 3))) & 0xFFu;
-    uint32_t other = mine;
-    permlane32_swap(mine, other);  // mine: run 2g (lanes 0-31), other: run 2g + 1 (lanes 32-63)
-    const uint32_t sh = 4 * h2;
-    bits |= (((mine >> sh) & 0xFu) | (((other >> sh) & 0xFu) << 4)) << (8 * g);
+    uint32_t r[4];
+    keep_counter(i0, g, h2, kj, h, b, r);
+#pragma unroll
+    for (int k = 0; k < 10; ++k) philox_round(r, a.seed_lo, a.seed_hi, k);
+    uint32_t lo, hi;
+    keep_compare(r, a.drop_thresh, kj & 7, lo, hi);
+    keep_gather(lo, hi);
+    bits |= keep_extract(lo, hi, kj & 7, h2) << (8 * g);
   }
   return bits;
+}
+
+// The same bits in 32 slices, for a tile whose hashing is spread over the
+// products of the tile before it (one slice per look-ahead product):
+// slice 8g + p of round g runs Philox rounds 2p, 2p + 1 (p < 5), the
+// comparisons (p = 5), the octet gather (p = 6) or the extraction (p = 7).
+struct KeepTask {
+  uint32_t c[4];
+  uint32_t lo, hi, bits;
+};
+
+__device__ __forceinline__ void dkdv_keep_slice(const BwdArgs& a, int b, int h, int i0, int h2, int kj,
+                                                KeepTask& k, int s) {
+  const int g = s >> 3, p = s & 7;
+  if (p == 0) {
+    keep_counter(i0, g, h2, kj, h, b, k.c);
+    if (g == 0) k.bits = 0;
+  }
+  if (p < 5) {
+    philox_round(k.c, a.seed_lo, a.seed_hi, 2 * p);
+    philox_round(k.c, a.seed_lo, a.seed_hi, 2 * p + 1);
+  } else if (p == 5) {
+    keep_compare(k.c, a.drop_thresh, kj & 7, k.lo, k.hi);
+  } else if (p == 6) {
+    keep_gather(k.lo, k.hi);
+  } else {
+    k.bits |= keep_extract(k.lo, k.hi, kj & 7, h2) << (8 * g);
+  }
 }
 
 // P, Z and dS of element r of a half (register r of S, dP: query
@@ -513,12 +565,12 @@ __device__ __forceinline__ f32x4 lds_f32x4(uint32_t addr) {
 // after look-ahead product i (the caller issues its tile loads there, so that
 // their issue overlaps the products).  On return sacc, pacc, zpk[0..3],
 // spk[0..3] describe the next half.
-template <int D, bool BF16, bool MASK, bool DROPOUT, typename Hook>
+template <int D, bool BF16, bool MASK, bool DROPOUT, typename Hook, typename Mid>
 __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st, f32x16& sacc, f32x16& pacc,
                                           uint32_t (&zpk)[8], uint32_t (&spk)[8], u32x4 (&pf)[4],
                                           const TileAddr& nop, const TileAddr& nnop, int nnqt, const TileAddr& tr,
                                           const HalfCtx& cur, const HalfCtx& nxt, int kj, int h2,
-                                          Hook&& hook) {
+                                          Hook&& hook, Mid&& mid) {
   using T = MTile<D, kBR>;
   constexpr int kNP = D / 8;  // look-ahead products (S and dP, D/16 k-steps each)
   constexpr int kPF = D >= 64 ? 4 : 2;  // LDS operand reads in flight (products ahead)
@@ -587,6 +639,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
   }
   const u32x4 zf[2] = {u32x4{zpk[0], zpk[1], zpk[2], zpk[3]}, u32x4{zpk[4], zpk[5], zpk[6], zpk[7]}};
   const u32x4 sf[2] = {u32x4{spk[0], spk[1], spk[2], spk[3]}, u32x4{spk[4], spk[5], spk[6], spk[7]}};
+  mid();  // the caller's work between the phases (it may complete nxt)
 
   // ---- phase 2: product j = (slice mm, head-dim tile dt, dV or dK) of h;
   // elements 0..7 of the next half, starting once ns, np are complete; the
@@ -853,11 +906,27 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     // products, LSE or D at product 1.
     const TileLoads x = tile_loads(tk3, (t + 3) % kNB);
     static_assert(4 * kNU - 2 < D / 8, "the look-ahead products must carry every tile load");
+    // Dropout: the next tile's keep bits, hashed in 32 slices spread over
+    // the look-ahead products of both halves (where the VALU has room next
+    // to the matrix cores); the second half's phase 2 reads them through n0.
+    KeepTask kt;
+    const int next_i0 = i_begin + max(tk1, 0) * kBR;
+    auto keep_hook = [&](int half, int i) __attribute__((always_inline)) {
+      if constexpr (DROPOUT) {
+        constexpr int kPer = (32 + 2 * (D / 8) - 1) / (2 * (D / 8));  // slices per look-ahead product
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int sl = (half * (D / 8) + i) * kPer + u;
+          if (sl < 32) dkdv_keep_slice(a, b, h, next_i0, h2, kj, kt, sl);
+        }
+      }
+    };
     auto load_hook = [&](int i) __attribute__((always_inline)) {
       if (i % 2 == 0 && i / 2 < 2 * kNU) tile_load_part(x, i / 2);
       if (i == 1) tile_load_part(x, 2 * kNU);
+      keep_hook(0, i);
     };
-    auto no_hook = [](int) {};
+    auto second_hook = [&](int i) __attribute__((always_inline)) { keep_hook(1, i); };
 
     const uint32_t qb = qs0 + buf * T::kBytes, gb = gs0 + buf * T::kBytes;
     const uint32_t nqb = qs0 + nbuf * T::kBytes, ngb = gs0 + nbuf * T::kBytes;
@@ -866,20 +935,25 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     uint32_t lb = ls0 + buf * kBR * 4 + 16 * h2, db = dls0 + buf * kBR * 4 + 16 * h2;
     uint32_t nlb = ls0 + nbuf * kBR * 4 + 16 * h2, ndb = dls0 + nbuf * kBR * 4 + 16 * h2;
     asm volatile("" : "+v"(lb), "+v"(db), "+v"(nlb), "+v"(ndb));
-    // keep bits of the next tile, whose first half the look-ahead reaches
-    uint32_t kb_next = 0;
-    if constexpr (DROPOUT) kb_next = dkdv_tile_keep(a, b, h, i_begin + max(tk1, 0) * kBR, h2, kj);
-    const HalfCtx h0{lb, db, i0, 0, kb_cur & 0xffffu}, h1{lb, db, i0, 1, kb_cur >> 16},
-        n0{nlb, ndb, i_begin + max(tk1, 0) * kBR, 0, kb_next & 0xffffu};
+    const HalfCtx h0{lb, db, i0, 0, kb_cur & 0xffffu}, h1{lb, db, i0, 1, kb_cur >> 16};
+    // first half of the next tile, whose keep bits the hooks finish before
+    // the second half's phase 2 reads them
+    HalfCtx n0{nlb, ndb, next_i0, 0, 0u};
     // On the last tile the look-ahead work reads a stale buffer and is
     // discarded; doing it anyway keeps the tile one basic block.  Masked
     // tiles come first, so the look-ahead into the next tile may use this
     // tile's masking.
     dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj, h2,
-                                       load_hook);
+                                       load_hook, []() {});
+    if constexpr (DROPOUT) {
+      // every slice ran in the first half and the second half's phase 1
+      static_assert(2 * (D / 8) * ((32 + 2 * (D / 8) - 1) / (2 * (D / 8))) >= 32, "keep slices do not fit");
+    }
     dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2,
-                                       no_hook);
-    kb_cur = kb_next;
+                                       second_hook, [&]() __attribute__((always_inline)) {
+                                         if constexpr (DROPOUT) n0.kb = kt.bits & 0xffffu;
+                                       });
+    if constexpr (DROPOUT) kb_cur = kt.bits;
   };
   // Causal: only the first two tiles (queries j0 .. j0+127) hold queries
   // before some key of the block, so only they are masked.

@@ -334,24 +334,28 @@ struct Philox4 {
   uint32_t x, y, z, w;
 };
 
+// Round r (0-based) of Philox-4x32-10 on the counter state c with key
+// (k0, k1): the round key is the key advanced r times by the Weyl constants.
+// Each 32x32 -> 64-bit product is one v_mad_u64_u32 (high and low halves),
+// each three-way xor one v_bitop3_b32.
+__device__ __forceinline__ void philox_round(uint32_t (&c)[4], uint32_t k0, uint32_t k1, int r) {
+  const uint32_t rk0 = k0 + (uint32_t)r * 0x9E3779B9u, rk1 = k1 + (uint32_t)r * 0xBB67AE85u;
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+  const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], rk0, 0x96);
+  const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], rk1, 0x96);
+  c[0] = n0;
+  c[1] = (uint32_t)p1;
+  c[2] = n2;
+  c[3] = (uint32_t)p0;
+}
+
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  uint32_t k0, uint32_t k1) {
+  uint32_t c[4] = {c0, c1, c2, c3};
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    // each 32x32 -> 64-bit product is one v_mad_u64_u32 (high and low halves),
-    // each three-way xor one v_bitop3_b32
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
-    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
-    c0 = n0;
-    c1 = (uint32_t)p1;
-    c2 = n2;
-    c3 = (uint32_t)p0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-  return {c0, c1, c2, c3};
+  for (int r = 0; r < 10; ++r) philox_round(c, k0, k1, r);
+  return {c[0], c[1], c[2], c[3]};
 }
 
 // Dropout keep decision of one element from its 16-bit Philox value: the
