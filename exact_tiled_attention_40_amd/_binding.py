@@ -21,7 +21,7 @@ FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 FA_MASK_BLOCK = 128       # rows and columns of one block-mask entry
 FA_MASK_MAX_N = 65536     # longest sequence the block-sparse calls accept
-FA_DECODE_MAX_Q = 4       # new query tokens per sequence in one decode step
+FA_DECODE_MAX_Q = 8       # new query tokens per sequence in one decode step
 _DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 
 

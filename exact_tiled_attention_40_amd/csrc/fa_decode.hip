@@ -272,7 +272,8 @@ template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_dec_c(const DecArgs& a, hipStream_t stream) {
   if (a.nq == 1) return launch_dec_q<D, BF16, CAUSAL, 1>(a, stream);
   if (a.nq == 2) return launch_dec_q<D, BF16, CAUSAL, 2>(a, stream);
-  return launch_dec_q<D, BF16, CAUSAL, 4>(a, stream);
+  if (a.nq <= 4) return launch_dec_q<D, BF16, CAUSAL, 4>(a, stream);
+  return launch_dec_q<D, BF16, CAUSAL, 8>(a, stream);
 }
 
 template <int D, bool BF16>

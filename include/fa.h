@@ -207,7 +207,7 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
  * a split kernel (one workgroup per sequence, head and 1024-key chunk) and a
  * merge kernel (log-sum-exp weighted sum of the chunks, the online-softmax
  * rule of section 3.2 of the lab write-up). */
-#define FA_DECODE_MAX_Q 4
+#define FA_DECODE_MAX_Q 8
 
 size_t fa_decode_workspace_size(int B, int H, int nq, int nk_max, int d);
 

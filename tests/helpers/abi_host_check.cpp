@@ -101,7 +101,7 @@ int main() {
   const size_t dneed = fa_decode_workspace_size(2, 4, 1, 3000, 128);
   CHECK(dneed > 0);
   CHECK(fa_decode(P, P, P, nullptr, P, F, 2, 4, 1, 3000, 128, 0.1f, 1, nullptr, 1, P, dneed) == FA_OK);
-  CHECK(fa_decode(P, P, P, nullptr, P, F, 2, 4, 5, 3000, 128, 0.1f, 1, nullptr, 1, P, dneed) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_decode(P, P, P, nullptr, P, F, 2, 4, 9, 3000, 128, 0.1f, 1, nullptr, 1, P, dneed) == FA_ERR_UNSUPPORTED);
   CHECK(fa_dropout_mask(static_cast<uint8_t*>(P), 0, 0, 16, 0.25f, 1, nullptr) == FA_OK && last_thresh == 16384u);
   for (int c = 0; c <= 8; ++c) CHECK(fa_strerror(c) != nullptr && std::strlen(fa_strerror(c)) > 0);
   std::printf("abi host check: clean (%d launches)\n", calls);

@@ -197,7 +197,7 @@ def test_decode_rejects_bad_arguments(lib):
         return lib.fa_decode(q, k, v, lens, o, lse, B, H, nq, nk, d, scale, causal, None, dtype, ws, wsb)
     assert call(q=None) == 1 and call(k=None) == 1 and call(lse=None) == 1
     assert call(B=0) == 2 and call(H=0) == 2 and call(nq=0) == 2 and call(nk=0) == 2
-    assert call(nq=5) == 3 and call(d=32) == 3 and call(d=96) == 3 and call(dtype=7) == 3
+    assert call(nq=9) == 3 and call(d=32) == 3 and call(d=96) == 3 and call(dtype=7) == 3
     assert call(scale=float("nan")) == 4 and call(scale=0.0) == 4
     assert call(q=P + 8) == 5 and call(lse=P + 4) == 5 and call(lens=P + 2) == 5
     assert call(ws=None) == 6 and call(wsb=need - 1) == 6

@@ -47,6 +47,11 @@ def wl(B, H, nq, nk, d, dtype, causal, seed):
     (2, 3, 2, 513, 128, "bf16", True),
     (1, 8, 3, 4097, 128, "f16", False),
     (4, 1, 4, 511, 64, "bf16", False),
+    # five to eight new tokens (speculative or chunked steps)
+    (2, 3, 5, 1100, 128, "bf16", True),
+    (3, 2, 8, 2500, 64, "f16", True),
+    (1, 4, 8, 300, 128, "f16", False),
+    (2, 2, 7, 6, 64, "bf16", True),
 ])
 def test_decode_small(B, H, nq, nk, d, dtype, causal):
     check(workloads.make_decode_inputs(wl(B, H, nq, nk, d, dtype, causal, seed=700 + nk)))
