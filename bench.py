@@ -3,6 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--block-density P] [--decode]
+    python bench.py --compare-standard [--seqlens 512,1024,...] [--dropout P]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 fa_forward (fused tiled forward) followed by the two backward kernels
@@ -245,6 +246,124 @@ def decode_bench(args) -> int:
     return 0
 
 
+def standard_attention_step(q, k, v, do, *, scale, causal, dropout_p=0.0, generator=None):
+    """Standard attention, forward then backward, with every intermediate
+    written out (the three-step method of the FlashAttention write-ups,
+    section 2.2 of the lab write-up): S = scale Q K^T and P = softmax(S) are
+    full N x N matrices per head, and the backward materialises dP and dS as
+    well.  torch eager ops in the inputs' dtype; this is the comparison side
+    of the measurement, not part of the library.
+
+    q, k, v, do: [B, N, H, d].  Returns (o, dq, dk, dv) in the same layout.
+    Dropout draws its own mask from torch's generator: it costs what a
+    materialised mask costs, but its bits are not the library's.  Operands of
+    the batched products are made contiguous first, transposes included."""
+    import torch
+    qh, kh, vh, doh = (t.permute(0, 2, 1, 3).contiguous() for t in (q, k, v, do))
+    n = qh.shape[2]
+    s = torch.matmul(qh, kh.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        hidden = torch.ones(n, n, dtype=torch.bool, device=s.device).triu_(1)
+        s.masked_fill_(hidden, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    if dropout_p > 0:
+        keep = torch.rand(p.shape, generator=generator, device=p.device) >= dropout_p
+        z = p * keep / (1.0 - dropout_p)
+    else:
+        z = p
+    o = torch.matmul(z, vh)
+    dv = torch.matmul(z.transpose(-1, -2).contiguous(), doh)
+    dz = torch.matmul(doh, vh.transpose(-1, -2).contiguous())
+    dp = dz * keep / (1.0 - dropout_p) if dropout_p > 0 else dz
+    ds = p * (dp - (p * dp).sum(dim=-1, keepdim=True))
+    dq = torch.matmul(ds, kh) * scale
+    dk = torch.matmul(ds.transpose(-1, -2).contiguous(), qh) * scale
+    return tuple(t.permute(0, 2, 1, 3) for t in (o, dq, dk, dv))
+
+
+def compare_standard(args) -> int:
+    """Tiled kernels against standard (materialised) attention, forward +
+    backward, at one or more sequence lengths of a fixed-length workload:
+    step time and peak device memory each side allocates beyond its inputs
+    (outputs, workspace and intermediates).  One JSON line per length."""
+    import torch
+    import exact_tiled_attention_40_amd as fa
+    import workloads
+
+    base = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+    if base.varlen or base.packed:
+        print("the standard-attention comparison runs on the fixed-length, unpacked workloads", file=sys.stderr)
+        return 2
+    if args.dropout >= 0:
+        base = dataclasses.replace(base, dropout_p=args.dropout)
+    lens = [int(s) for s in args.seqlens.split(",")] if args.seqlens else [base.N]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(base.seed)
+    for n in lens:
+        wl = dataclasses.replace(base, N=n, name=base.name.replace(f"_N{base.N}_", f"_N{n}_"))
+        x = workloads.make_inputs(wl)
+        q, k, v, do = (t.to(dev) for t in (x.q, x.k, x.v, x.do))
+        kw = dict(scale=wl.scale, causal=wl.causal, dropout_p=wl.dropout_p, seed=wl.seed)
+
+        def tiled():
+            o, lse = fa.fa_forward(q, k, v, stream=stream, **kw)
+            grads = fa.fa_backward(q, k, v, o, lse, do, stream=stream, **kw)
+            return (o,) + tuple(grads)
+
+        def standard():
+            return standard_attention_step(q, k, v, do, scale=wl.scale, causal=wl.causal,
+                                           dropout_p=wl.dropout_p, generator=gen)
+
+        res = {}
+        outs = {}
+        for name, fn in (("tiled", tiled), ("standard", standard)):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            held = torch.cuda.memory_allocated()
+            outs[name] = fn()
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated() - held
+            outs[name] = tuple(t.float() for t in outs[name]) if wl.dropout_p == 0 else None
+            t_settle = time.perf_counter()
+            while True:
+                for _ in range(max(args.warmup, 1)):
+                    fn()
+                torch.cuda.synchronize()
+                if time.perf_counter() - t_settle >= args.settle_s:
+                    break
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = {"ms_per_step": e0.elapsed_time(e1) / args.steps, "peak_bytes": int(peak)}
+        pairs = visible_pairs(wl)
+        flops = 14.0 * wl.d * pairs
+        for r in res.values():
+            r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
+        line = {
+            "metric": "standard attention vs tiled attention, fwd+bwd step (speedup, memory ratio)",
+            "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": n, "d": wl.d, "causal": wl.causal,
+                       "dropout_p": wl.dropout_p, "dtype": wl.dtype},
+            "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+            "tiled": res["tiled"], "standard": res["standard"],
+            "speedup": res["standard"]["ms_per_step"] / res["tiled"]["ms_per_step"],
+            "memory_ratio": res["standard"]["peak_bytes"] / max(res["tiled"]["peak_bytes"], 1),
+        }
+        if outs["tiled"] is not None:
+            # both sides compute the same attention (no dropout): largest
+            # relative difference of each output, a check on the comparison
+            line["max_rel_diff"] = {nm: float((a - b).abs().max() / b.abs().max().clamp_min(1e-30))
+                                    for nm, a, b in zip(("o", "dq", "dk", "dv"), outs["tiled"], outs["standard"])}
+        print(json.dumps(line), flush=True)
+        del q, k, v, do, x, outs
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +385,12 @@ def main() -> int:
                     help="run the chosen workload with this head size instead (32, 64, 96 or 128)")
     ap.add_argument("--settle-s", type=float, default=1.5,
                     help="repeat the warm-up steps until this many seconds have passed (clock settling)")
+    ap.add_argument("--compare-standard", action="store_true",
+                    help="time standard (materialised) attention against the tiled kernels instead: step time "
+                         "and peak memory, one JSON line per sequence length")
+    ap.add_argument("--seqlens", default="", help="comma-separated sequence lengths for --compare-standard")
+    ap.add_argument("--dropout", type=float, default=-1.0,
+                    help="dropout probability for --compare-standard (default: the workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels shard by (batch, head) "
@@ -279,6 +404,8 @@ def main() -> int:
 
     if args.decode:
         return decode_bench(args)
+    if args.compare_standard:
+        return compare_standard(args)
 
     import torch
     import exact_tiled_attention_40_amd as fa
