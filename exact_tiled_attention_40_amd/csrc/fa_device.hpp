@@ -37,19 +37,6 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// D += A * B on a 16x16 tile with a K slice of 32.  Lane l holds A row
-// l%16, B column l%16 and one group of eight K elements (group l/16); the
-// accumulator register r of lane l is element (row 4*(l/16) + r, column l%16).
-template <bool BF16>
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
 // Two fp32 values -> two 16-bit floats (round to nearest even) in one word.
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -66,20 +53,6 @@ template <bool BF16>
 __device__ __forceinline__ float to_f32(uint16_t x) {
   if constexpr (BF16) return __builtin_bit_cast(float, (uint32_t)x << 16);
   else return (float)__builtin_bit_cast(_Float16, x);
-}
-
-// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// source lane s supplies the address of four consecutive 16-bit elements;
-// destination lane l receives element l%4 of source lanes 4e + l/4 (e = 0..3).
-// Pointed at a row-major [k][n] tile with lane s addressing row k0 + s/4,
-// columns n0 + 4*(s%4) .. +3, lane l gets column n0 + l%16, rows k0 .. k0+3.
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-__device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
 }
 
 // Buffer resource over `bytes` bytes from `base`: raw buffer loads at
@@ -181,6 +154,11 @@ __device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
   return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)addr;
 }
 
+// LDS transpose read (ds_read_b64_tr_b16) at a byte address.  Within each group of 16 lanes,
+// source lane s supplies the address of four consecutive 16-bit elements;
+// destination lane l receives element l%4 of source lanes 4e + l/4 (e = 0..3).
+// Pointed at a row-major [k][n] tile with lane s addressing row k0 + s/4,
+// columns n0 + 4*(s%4) .. +3, lane l gets column n0 + l%16, rows k0 .. k0+3.
 __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
   return __builtin_bit_cast(u32x2, v);
