@@ -197,12 +197,13 @@ def decode_bench(args) -> int:
                      stream=stream)
 
     t_settle = time.perf_counter()
-    while True:
-        for _ in range(max(args.warmup, 1)):
-            step()
-        torch.cuda.synchronize()
-        if time.perf_counter() - t_settle >= args.settle_s:
-            break
+    with ClockSampler() as clock:
+        while True:
+            for _ in range(max(args.warmup, 1)):
+                step()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_settle >= args.settle_s:
+                break
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
@@ -229,6 +230,7 @@ def decode_bench(args) -> int:
                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": ms,
                      "algorithmic_bytes_per_launch": algo},
         "wall_s_timed": wall,
+        "observed_sclk_mhz": clock.summary(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -244,6 +246,60 @@ def decode_bench(args) -> int:
                                           "kernel's 16-bit cache bytes)"}
     print(json.dumps(line), flush=True)
     return 0
+
+
+class ClockSampler:
+    """Samples the GPU shader clock (the current level of sysfs pp_dpm_sclk,
+    the line marked '*') from a thread while the warm-up steps run, which are
+    the same steps the timed region runs.  Reports the median, minimum and
+    maximum in MHz once the clock has ramped up, or None where there is not
+    exactly one such file."""
+
+    def __init__(self, period_s: float = 0.05):
+        import glob
+        import threading
+        files = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+        self.path = files[0] if len(files) == 1 else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if self.path else None
+
+    def _read(self):
+        try:
+            with open(self.path) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._thread:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        """Over the second half of the samples: the first ones catch the
+        clock still ramping up from idle."""
+        if not self.samples:
+            return None
+        v = sorted(self.samples[len(self.samples) // 2:])
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
+                "source": "sysfs pp_dpm_sclk current level, second half of the warm-up steps"}
 
 
 def standard_attention_step(q, k, v, do, *, scale, causal, dropout_p=0.0, generator=None):
@@ -462,12 +518,13 @@ def main() -> int:
     # the GPU clocks take about a second of load to settle, and a step is
     # under a millisecond.
     t_settle = time.perf_counter()
-    while True:
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        if time.perf_counter() - t_settle >= args.settle_s or args.warmup == 0:
-            break
+    with ClockSampler() as clock:
+        while True:
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_settle >= args.settle_s or args.warmup == 0:
+                break
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -530,6 +587,7 @@ def main() -> int:
         "bwd": {"tflops": bwd_tflops, "ms": bwd_ms, "frac": bwd_tflops / PEAK_TFLOPS},
         "kernels": per_kernel,
         "wall_s_timed": wall,
+        "observed_sclk_mhz": clock.summary(),
         "roofline": roofline,
         "cpu_baseline": None,
     }
