@@ -2,7 +2,7 @@
 """Attention forward + backward throughput on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--block-density P] [--decode]
+                    [--block-density P] [--decode [--page-size P]]
     python bench.py --compare-standard [--seqlens 512,1024,...] [--dropout P]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
@@ -189,12 +189,25 @@ def decode_bench(args) -> int:
     lens = x.seqlens.to(dev) if x.seqlens is not None else None
     o = torch.empty_like(q)
     lse = torch.empty((wl.B, wl.nq, wl.H), dtype=torch.float32, device=dev)
-    ws = torch.empty(fa.fa_decode_workspace_size(wl.B, wl.H, wl.nq, wl.nk, wl.d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.page_size:
+        # the same caches as a paged cache: shuffled pool pages and a block table
+        kp, vp, table = workloads.paged_cache(x.k, x.v, args.page_size, seed=wl.seed + 1,
+                                              lengths=None if x.seqlens is None else x.seqlens.tolist())
+        kp, vp, table = kp.to(dev), vp.to(dev), table.to(dev)
+        del k, v
+        cap = table.shape[1] * args.page_size
+        ws = torch.empty(fa.fa_decode_workspace_size(wl.B, wl.H, wl.nq, cap, wl.d), dtype=torch.uint8, device=dev)
 
-    def step():
-        fa.fa_decode(q, k, v, seqlens_k=lens, scale=wl.scale, causal=wl.causal, out=o, lse=lse, workspace=ws,
-                     stream=stream)
+        def step():
+            fa.fa_decode_paged(q, kp, vp, table, seqlens_k=lens, scale=wl.scale, causal=wl.causal, out=o, lse=lse,
+                               workspace=ws, stream=stream)
+    else:
+        ws = torch.empty(fa.fa_decode_workspace_size(wl.B, wl.H, wl.nq, wl.nk, wl.d), dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.fa_decode(q, k, v, seqlens_k=lens, scale=wl.scale, causal=wl.causal, out=o, lse=lse, workspace=ws,
+                         stream=stream)
 
     t_settle = time.perf_counter()
     with ClockSampler() as clock:
@@ -224,9 +237,11 @@ def decode_bench(args) -> int:
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "nq": wl.nq, "nk": wl.nk, "d": wl.d,
-                   "causal": wl.causal, "valid_cache_tokens": valid},
-        "roofline": {"bound": "hbm", "kernel": "fa_decode (split + merge)", "achieved": gbs, "peak": PEAK_HBM_GBS,
+        "config": {"workload": wl.name + (f"_paged{args.page_size}" if args.page_size else ""), "B": wl.B, "H": wl.H,
+                   "nq": wl.nq, "nk": wl.nk, "d": wl.d, "causal": wl.causal, "valid_cache_tokens": valid,
+                   **({"page_size": args.page_size} if args.page_size else {})},
+        "roofline": {"bound": "hbm", "kernel": "fa_decode_paged (split + merge)" if args.page_size
+                     else "fa_decode (split + merge)", "achieved": gbs, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": ms,
                      "algorithmic_bytes_per_launch": algo},
         "wall_s_timed": wall,
@@ -445,6 +460,9 @@ def main() -> int:
                          "(diagonal blocks kept); 0 = dense")
     ap.add_argument("--decode", action="store_true",
                     help="time fa_decode (KV-cache decode step) on a decode workload instead")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="with --decode: time fa_decode_paged on the same caches split into pages of this many "
+                         "tokens (a power of two) in shuffled order")
     ap.add_argument("--head-dim", type=int, default=0,
                     help="run the chosen workload with this head size instead (32, 64, 96 or 128)")
     ap.add_argument("--settle-s", type=float, default=1.5,

@@ -59,6 +59,8 @@ def _load():
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
     lib.fa_decode.restype = i
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
+    lib.fa_decode_paged.restype = i
     lib.fa_dropout_mask.argtypes = [vp, i, i, i, f, u64, vp]
     lib.fa_dropout_mask.restype = i
     lib.fa_strerror.argtypes = [i]
@@ -254,4 +256,43 @@ def fa_decode(q, k_cache, v_cache, *, seqlens_k=None, scale=None, causal=False, 
     _check(_lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(out), _ptr(lse), B, H, nq,
                           nk, d, float(scale), int(bool(causal)), _stream(stream), _DTYPES[q.dtype], _ptr(workspace),
                           workspace.numel() * workspace.element_size()))
+    return out, lse
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, *, seqlens_k=None, scale=None, causal=False, out=None,
+                    lse=None, workspace=None, stream=None):
+    """One KV-cache decode step over a paged cache.  q [B, nq, H, d];
+    k_pages, v_pages [num_pages, page_size, H, d] (contiguous, page_size a
+    power of two); block_table int32 [B, max_pages] on the device (cache
+    position j of sequence b is token j % page_size of page
+    block_table[b, j // page_size]); seqlens_k optional int32 [B] on the
+    device.  Returns (o [B, nq, H, d], lse float32 [B, nq, H])."""
+    if q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise FAError(3, fa_strerror(3))
+    for t in (q, k_pages, v_pages):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("q, k_pages and v_pages must be contiguous 4-d tensors")
+    B, nq, H, d = q.shape
+    num_pages, page_size = k_pages.shape[:2]
+    if tuple(k_pages.shape) != (num_pages, page_size, H, d) or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages, v_pages must be [num_pages, page_size, H, d] with q's H, d")
+    if (block_table.dtype != torch.int32 or not block_table.is_cuda or block_table.dim() != 2
+            or block_table.shape[0] != B or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 device tensor [B, max_pages]")
+    max_pages = block_table.shape[1]
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or not seqlens_k.is_cuda or seqlens_k.numel() != B):
+        raise ValueError("seqlens_k must be an int32 device tensor of B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, nq, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, fa_decode_workspace_size(B, H, nq, max_pages * page_size, d)),
+                                dtype=torch.uint8, device=q.device)
+    _check(_lib.fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
+                                _ptr(lse), B, H, nq, num_pages, page_size, max_pages, d, float(scale),
+                                int(bool(causal)), _stream(stream), _DTYPES[q.dtype], _ptr(workspace),
+                                workspace.numel() * workspace.element_size()))
     return out, lse

@@ -189,6 +189,36 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                    const int32_t* seqlens_k, void* o, float* lse, int B, int H, int nq, int num_pages,
+                    int page_size, int max_pages, int d, float scale, int causal, void* stream, int dtype,
+                    void* workspace, size_t workspace_bytes) {
+  if (!q || !k_pages || !v_pages || !block_table || !o || !lse) return FA_ERR_NULL_POINTER;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || nq < 1 || num_pages < 1 || max_pages < 1 || page_size < 1) return FA_ERR_BAD_SHAPE;
+  if (page_size & (page_size - 1)) return FA_ERR_UNSUPPORTED;
+  if (nq > FA_DECODE_MAX_Q) return FA_ERR_UNSUPPORTED;
+  const int64_t capacity = (int64_t)max_pages * page_size;
+  if (capacity > INT32_MAX || (int64_t)B * max_pages > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  const int nk_max = (int)capacity;
+  if ((int64_t)B * H * fa::decode_splits(nk_max) > INT32_MAX || (int64_t)B * nq * H > INT32_MAX)
+    return FA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGNMENT;
+  if (reinterpret_cast<uintptr_t>(block_table) & 3u) return FA_ERR_ALIGNMENT;
+  if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u)) return FA_ERR_ALIGNMENT;
+  const size_t need = fa_decode_workspace_size(B, H, nq, nk_max, d);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGNMENT;
+  fa::DecodeShape s{B, H, nq, nk_max, d, causal != 0, dtype == FA_DTYPE_BF16, scale};
+  const fa::DecodePages pages{block_table, page_size, max_pages, num_pages};
+  const hipError_t e = fa::launch_decode(s, q, k_pages, v_pages, seqlens_k, o, lse, static_cast<float*>(workspace),
+                                         static_cast<hipStream_t>(stream), &pages);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed, void* stream) {
   if (!keep) return FA_ERR_NULL_POINTER;
   if (b < 0 || h < 0 || N < 1 || (int64_t)N * N > ((int64_t)1 << 40)) return FA_ERR_BAD_SHAPE;

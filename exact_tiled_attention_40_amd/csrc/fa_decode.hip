@@ -35,6 +35,11 @@ struct DecArgs {
   float* part_o;      // [B*H, nsplit, nq, d]
   float* part_m;      // [B*H, nsplit, nq] (log2 units)
   float* part_l;      // [B*H, nsplit, nq]
+  // paged cache: k and v are pools of num_pages pages of page_size tokens
+  // ([num_pages, page_size, H, d]); cache position j of sequence b is token
+  // j % page_size of page table[b * max_pages + j / page_size]
+  const int32_t* table;
+  int page_size, page_shift, max_pages, num_pages;
   int B, H, nq, nk, nsplit;
   float scale_log2;
 };
@@ -50,7 +55,7 @@ __device__ __forceinline__ void unpack8(u32x4 x, float (&f)[8]) {
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-template <int D, bool BF16, bool CAUSAL, int NQ>
+template <int D, bool BF16, bool CAUSAL, int NQ, bool PAGED>
 __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecArgs a) {
   constexpr int kSl = D / 8;                // lanes per key row
   constexpr int kRows = kDecThreads / kSl;  // key rows per pass
@@ -70,8 +75,30 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecArgs a)
   const int n = max(0, min(L, j0 + kDecChunk) - j0);  // keys of this chunk
   const int nq = a.nq;
   const int64_t row = (int64_t)a.H * D;               // elements between tokens
-  const uint16_t* kb = a.k + ((int64_t)b * a.nk + j0) * row + (int64_t)h * D + 8 * c;
-  const uint16_t* vb = a.v + ((int64_t)b * a.nk + j0) * row + (int64_t)h * D + 8 * c;
+  const int64_t base = PAGED ? 0 : ((int64_t)b * a.nk + j0) * row;
+  const uint16_t* kb = a.k + base + (int64_t)h * D + 8 * c;
+  const uint16_t* vb = a.v + base + (int64_t)h * D + 8 * c;
+  // Paged: the chunk's page numbers, staged in LDS once so that no key load
+  // waits on a table load; clamped into the pool, so every read stays in
+  // bounds whatever the table holds.  Only the pages of the chunk's valid
+  // keys are read from the table.
+  __shared__ int pg[PAGED ? kDecChunk : 1];
+  const int fp = PAGED ? j0 >> a.page_shift : 0;  // first page of the chunk
+  if constexpr (PAGED) {
+    const int npg = n > 0 ? ((j0 + n - 1) >> a.page_shift) - fp + 1 : 0;
+    for (int i = tid; i < npg; i += kDecThreads)
+      pg[i] = min(max(a.table[(int64_t)b * a.max_pages + fp + i], 0), a.num_pages - 1);
+    __syncthreads();
+  }
+  // element offset of chunk row r (0 <= r < n) from kb / vb
+  auto roff = [&](int r) __attribute__((always_inline)) -> int64_t {
+    if constexpr (PAGED) {
+      const int j = j0 + r;
+      return ((int64_t)pg[(j >> a.page_shift) - fp] * a.page_size + (j & (a.page_size - 1))) * row;
+    } else {
+      return (int64_t)r * row;
+    }
+  };
 
   // this lane's slice of every query, prescaled by scale * log2(e)
   float qv[NQ][8];
@@ -94,7 +121,7 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecArgs a)
 #pragma unroll
     for (int u = 0; u < kDecBatch; ++u) {
       const int r = r0 + u * kRows + g;
-      kx[u] = r < n ? load16(kb + (int64_t)r * row) : u32x4{0u, 0u, 0u, 0u};
+      kx[u] = r < n ? load16(kb + roff(r)) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kDecBatch; ++u) {
@@ -170,7 +197,7 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecArgs a)
 #pragma unroll
     for (int u = 0; u < kDecBatch; ++u) {
       const int r = r0 + u * kRows + g;
-      vx[u] = r < n ? load16(vb + (int64_t)r * row) : u32x4{0u, 0u, 0u, 0u};
+      vx[u] = r < n ? load16(vb + roff(r)) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kDecBatch; ++u) {
@@ -262,8 +289,12 @@ hipError_t launch_dec_q(const DecArgs& a, hipStream_t stream) {
   const int64_t nsplitwg = (int64_t)a.B * a.H * a.nsplit;
   const int64_t nmerge = (int64_t)a.B * a.nq * a.H;
   if (nsplitwg > 0x7fffffff || nmerge > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16, CAUSAL, NQ>), dim3((unsigned)nsplitwg), dim3(kDecThreads), 0,
-                     stream, a);
+  if (a.table)
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16, CAUSAL, NQ, true>), dim3((unsigned)nsplitwg),
+                       dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16, CAUSAL, NQ, false>), dim3((unsigned)nsplitwg),
+                       dim3(kDecThreads), 0, stream, a);
   hipLaunchKernelGGL((fa_decode_merge_kernel<D, BF16>), dim3((unsigned)nmerge), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
@@ -286,8 +317,13 @@ hipError_t launch_dec_d(const DecodeShape& s, const DecArgs& a, hipStream_t stre
 int decode_splits(int nk) { return (nk + kDecChunk - 1) / kDecChunk; }
 
 hipError_t launch_decode(const DecodeShape& s, const void* q, const void* k, const void* v, const int32_t* lk,
-                         void* o, float* lse, float* workspace, hipStream_t stream) {
+                         void* o, float* lse, float* workspace, hipStream_t stream, const DecodePages* pages) {
   DecArgs a;
+  a.table = pages ? pages->table : nullptr;
+  a.page_size = pages ? pages->page_size : 1;
+  a.page_shift = pages ? __builtin_ctz((unsigned)pages->page_size) : 0;
+  a.max_pages = pages ? pages->max_pages : 0;
+  a.num_pages = pages ? pages->num_pages : 0;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);

@@ -46,8 +46,17 @@ struct DecodeShape {
 int decode_splits(int nk);
 
 // workspace: fp32, B*H*decode_splits(nk)*nq*(d + 2) floats.
+// A paged cache: pools of num_pages pages of page_size tokens (a power of
+// two) and a device table [B, max_pages] of page numbers; nk of the shape is
+// max_pages * page_size.
+struct DecodePages {
+  const int32_t* table;
+  int page_size, max_pages, num_pages;
+};
+
 hipError_t launch_decode(const DecodeShape& s, const void* q, const void* k, const void* v, const int32_t* lk,
-                         void* o, float* lse, float* workspace, hipStream_t stream);
+                         void* o, float* lse, float* workspace, hipStream_t stream,
+                         const DecodePages* pages = nullptr);
 
 hipError_t launch_dropout_mask(uint8_t* keep, int b, int h, int N, uint32_t thresh, uint64_t seed,
                                hipStream_t stream);

@@ -215,6 +215,33 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
               void* o, float* lse, int B, int H, int nq, int nk_max, int d, float scale,
               int causal, void* stream, int dtype, void* workspace, size_t workspace_bytes);
 
+/* The same decode step over a paged cache: the keys and values of all
+ * sequences live in two pools of fixed-size pages, and a block table maps
+ * each sequence's cache positions to pages, so that caches can grow page by
+ * page without being copied.  The attention computed is exactly that of
+ * fa_decode on the cache the table describes.
+ *   k_pages,
+ *   v_pages     : [num_pages, page_size, H, d] contiguous (16-byte aligned).
+ *   block_table : DEVICE int32 [B, max_pages]: cache position j of sequence
+ *                 b is token j % page_size of page
+ *                 block_table[b * max_pages + j / page_size].  Only the
+ *                 entries covering positions below seqlens_k[b] are read.
+ *                 Entries must lie in [0, num_pages); an entry outside is
+ *                 clamped into that range (every read stays inside the
+ *                 pools, the output is then unspecified).
+ *   seqlens_k   : DEVICE int32 [B] or NULL (every sequence holds
+ *                 max_pages * page_size tokens); clamped to
+ *                 [0, max_pages * page_size].
+ *   page_size   : a power of two.
+ * q, o, lse, causal, scale, dtype and the limits on nq and d are those of
+ * fa_decode; the workspace is fa_decode_workspace_size(B, H, nq,
+ * max_pages * page_size, d) bytes.  Errors as for fa_decode, and
+ * FA_ERR_UNSUPPORTED for a page size that is not a power of two. */
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                    const int32_t* seqlens_k, void* o, float* lse, int B, int H, int nq, int num_pages,
+                    int page_size, int max_pages, int d, float scale, int causal, void* stream, int dtype,
+                    void* workspace, size_t workspace_bytes);
+
 /* Dropout keep mask of a single (b, h) head as the fused kernels draw it:
  * keep[i * N + j] = 1 if element (i, j) is kept, 0 if dropped, for
  * 0 <= i, j < N (both local indices; causal masking is NOT applied).  keep

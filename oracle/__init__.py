@@ -215,6 +215,32 @@ def decode(q, k_cache, v_cache, *, scale: float, causal: bool, seqlens_k=None):
     return o, lse
 
 
+def decode_paged(q, k_pages, v_pages, block_table, *, scale: float, causal: bool, seqlens_k=None):
+    """The decode step over a paged cache: k_pages, v_pages [num_pages, P,
+    H, d] hold pages of P tokens, and cache position j of sequence b is token
+    j % P of page block_table[b][j // P].  Gathers each sequence's valid
+    positions (all max_pages * P if seqlens_k is None) into the contiguous
+    [B, nk_max, H, d] layout and runs decode() on it; table entries past a
+    sequence's length are not used."""
+    kp = np.asarray(k_pages, dtype=np.float64)
+    vp = np.asarray(v_pages, dtype=np.float64)
+    table = np.asarray(block_table, dtype=np.int64)
+    B, max_pages = table.shape
+    P = kp.shape[1]
+    nk = max_pages * P
+    lens = np.full(B, nk, dtype=np.int64) if seqlens_k is None else np.clip(np.asarray(seqlens_k), 0, nk)
+    k = np.zeros((B, nk) + kp.shape[2:])
+    v = np.zeros_like(k)
+    for b in range(B):
+        pos = np.arange(lens[b])
+        page = table[b, pos // P]
+        if len(page) and (page.min() < 0 or page.max() >= kp.shape[0]):
+            raise ValueError("block table entry outside the page pool")
+        k[b, :lens[b]] = kp[page, pos % P]
+        v[b, :lens[b]] = vp[page, pos % P]
+    return decode(q, k, v, scale=scale, causal=causal, seqlens_k=lens.astype(np.int32))
+
+
 def rows_head(q, k, v, dout=None, *, scale: float, causal: bool, rows):
     """O, LSE (and dQ if dout is given) of the listed query rows of one head,
     without forming P: q, k, v, dout float64 [L, d] (any row stride).

@@ -18,6 +18,8 @@ fa::AttnShape last{};
 int last_stages = 0;
 const float *last_delta = nullptr, *last_lse2 = nullptr;
 uint32_t last_thresh = 0;
+fa::DecodeShape last_dec{};
+fa::DecodePages last_pages{};
 }  // namespace
 
 namespace fa {
@@ -36,9 +38,11 @@ hipError_t launch_backward(const AttnShape& s, const void*, const void*, const v
   return hipSuccess;
 }
 int decode_splits(int nk) { return (nk + 1023) / 1024; }
-hipError_t launch_decode(const DecodeShape&, const void*, const void*, const void*, const int32_t*, void*, float*,
-                         float*, hipStream_t) {
+hipError_t launch_decode(const DecodeShape& s, const void*, const void*, const void*, const int32_t*, void*, float*,
+                         float*, hipStream_t, const DecodePages* pages) {
   ++calls;
+  last_dec = s;
+  last_pages = pages ? *pages : DecodePages{nullptr, 0, 0, 0};
   return hipSuccess;
 }
 hipError_t launch_dropout_mask(uint8_t*, int, int, int, uint32_t thresh, uint64_t, hipStream_t) {
@@ -102,6 +106,22 @@ int main() {
   CHECK(dneed > 0);
   CHECK(fa_decode(P, P, P, nullptr, P, F, 2, 4, 1, 3000, 128, 0.1f, 1, nullptr, 1, P, dneed) == FA_OK);
   CHECK(fa_decode(P, P, P, nullptr, P, F, 2, 4, 9, 3000, 128, 0.1f, 1, nullptr, 1, P, dneed) == FA_ERR_UNSUPPORTED);
+  CHECK(last_pages.table == nullptr);
+  // paged decode: capacity = max_pages * page_size, the table reaches the launcher
+  const int32_t* tbl = static_cast<const int32_t*>(P);
+  const size_t pneed = fa_decode_workspace_size(2, 4, 3, 47 * 64, 128);
+  CHECK(fa_decode_paged(P, P, P, tbl, nullptr, P, F, 2, 4, 3, 100, 64, 47, 128, 0.1f, 1, nullptr, 1, P, pneed) ==
+        FA_OK);
+  CHECK(last_dec.nk == 47 * 64 && last_dec.nq == 3 && last_pages.table == tbl && last_pages.page_size == 64 &&
+        last_pages.max_pages == 47 && last_pages.num_pages == 100);
+  CHECK(fa_decode_paged(P, P, P, tbl, nullptr, P, F, 2, 4, 3, 100, 64, 47, 128, 0.1f, 1, nullptr, 1, P,
+                        pneed - 1) == FA_ERR_WORKSPACE);
+  CHECK(fa_decode_paged(P, P, P, tbl, nullptr, P, F, 2, 4, 3, 100, 48, 47, 128, 0.1f, 1, nullptr, 1, P, pneed) ==
+        FA_ERR_UNSUPPORTED);
+  CHECK(fa_decode_paged(P, P, P, nullptr, nullptr, P, F, 2, 4, 3, 100, 64, 47, 128, 0.1f, 1, nullptr, 1, P,
+                        pneed) == FA_ERR_NULL_POINTER);
+  CHECK(fa_decode_paged(P, P, P, tbl + 0, nullptr, P, F, 2, 4, 3, 100, 1 << 30, 4, 128, 0.1f, 1, nullptr, 1, P,
+                        pneed) == FA_ERR_BAD_SHAPE);
   CHECK(fa_dropout_mask(static_cast<uint8_t*>(P), 0, 0, 16, 0.25f, 1, nullptr) == FA_OK && last_thresh == 16384u);
   for (int c = 0; c <= 8; ++c) CHECK(fa_strerror(c) != nullptr && std::strlen(fa_strerror(c)) > 0);
   std::printf("abi host check: clean (%d launches)\n", calls);

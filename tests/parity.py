@@ -92,7 +92,7 @@ def rel_fro(x: Inputs, g_gpu, g_ref, pairs, floor_ref=None):
 
     A gradient can vanish exactly (dQ and dK when a row sees a single key);
     then the denominator is floored at ||floor_ref||_F (the dV reference, the
-    scale of the gradients), so rounding noise is judged against that scale."""
+    scale of the gradients), so rounding noise is measured against that scale."""
     g = tokens_f64(g_gpu)
     num = den = fden = 0.0
     worst = 0.0

@@ -29,8 +29,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage", "fa_backward_stage",
-        "fa_backward_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_dropout_mask", "fa_forward",
-        "fa_forward_block_sparse", "fa_strerror"])
+        "fa_backward_workspace_size", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size", "fa_dropout_mask",
+        "fa_forward", "fa_forward_block_sparse", "fa_strerror"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -60,6 +60,7 @@ def lib():
     L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_decode_workspace_size.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
+    L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     return L
@@ -202,6 +203,22 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(q=P + 8) == 5 and call(lse=P + 4) == 5 and call(lens=P + 2) == 5
     assert call(ws=None) == 6 and call(wsb=need - 1) == 6
     assert call(ws=P + 4) == 5
+
+
+def test_decode_paged_rejects_bad_arguments(lib):
+    need = lib.fa_decode_workspace_size(1, 2, 1, 16 * 64, 128)
+
+    def call(q=P, k=P, v=P, table=P, lens=None, o=P, lse=P, B=1, H=2, nq=1, num_pages=20, page_size=64,
+             max_pages=16, d=128, scale=0.1, causal=0, dtype=1, ws=P, wsb=need):
+        return lib.fa_decode_paged(q, k, v, table, lens, o, lse, B, H, nq, num_pages, page_size, max_pages, d, scale,
+                                   causal, None, dtype, ws, wsb)
+    assert call(table=None) == 1 and call(k=None) == 1 and call(o=None) == 1
+    assert call(num_pages=0) == 2 and call(page_size=0) == 2 and call(max_pages=0) == 2 and call(B=0) == 2
+    assert call(page_size=48) == 3 and call(page_size=3) == 3 and call(nq=9) == 3 and call(d=96) == 3
+    assert call(page_size=1 << 30, max_pages=4) == 2          # capacity above 2^31 - 1 tokens
+    assert call(table=P + 2) == 5 and call(lens=P + 2) == 5 and call(v=P + 8) == 5
+    assert call(wsb=need - 1) == 6 and call(ws=None) == 6
+    assert call(scale=float("inf")) == 4
 
 
 def test_abi_front_end_under_sanitizers(tmp_path):

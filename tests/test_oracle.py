@@ -556,6 +556,49 @@ def test_decode_queries_that_see_no_key():
     assert np.isclose(lse[0, 2, 0], 0.5 * float(q[0, 2, 0] @ kc[0, 0, 0]), atol=1e-14)
 
 
+def paged_from_contiguous(kc, P, rng, spare=3):
+    """Scatter a contiguous [B, nk, H, d] cache into a shuffled page pool:
+    page p of sequence b goes to pool slot perm[b * max_pages + p]; `spare`
+    unused slots hold NaN.  Returns (pool, table)."""
+    B, nk, H, d = kc.shape
+    max_pages = nk // P
+    n = B * max_pages + spare
+    perm = rng.permutation(n)
+    pool = np.full((n, P, H, d), np.nan)
+    table = np.zeros((B, max_pages), dtype=np.int32)
+    for b in range(B):
+        for p in range(max_pages):
+            slot = perm[b * max_pages + p]
+            pool[slot] = kc[b, p * P:(p + 1) * P]
+            table[b, p] = slot
+    return pool, table
+
+
+@pytest.mark.parametrize("P,causal", [(4, False), (8, True), (1, True), (32, False)])
+def test_decode_paged_equals_contiguous_decode(P, causal):
+    # the cache scattered page by page into a shuffled pool (with unused NaN
+    # pages, and table entries past each length set to -1) decodes exactly as
+    # the contiguous cache does
+    B, H, d, nq, nk = 3, 2, 8, 3, 32
+    q, kc, vc = rnd((B, nq, H, d), 630), rnd((B, nk, H, d), 631), rnd((B, nk, H, d), 632)
+    lens = np.array([32, 13, 0], dtype=np.int32)
+    rng = np.random.default_rng(P)
+    kp, table = paged_from_contiguous(kc, P, rng)
+    vp, table_v = paged_from_contiguous(vc, P, np.random.default_rng(P))
+    assert (table == table_v).all()
+    for b in range(B):
+        table[b, (lens[b] + P - 1) // P:] = -1
+    o_ref, lse_ref = oracle.decode(q, kc, vc, scale=0.4, causal=causal, seqlens_k=lens)
+    o, lse = oracle.decode_paged(q, kp, vp, table, scale=0.4, causal=causal, seqlens_k=lens)
+    assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+
+
+def test_decode_paged_rejects_entries_outside_the_pool():
+    q, kp, vp = rnd((1, 1, 1, 4), 640), rnd((2, 4, 1, 4), 641), rnd((2, 4, 1, 4), 642)
+    with pytest.raises(ValueError):
+        oracle.decode_paged(q, kp, vp, np.array([[0, 2]], dtype=np.int32), scale=1.0, causal=False)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_rows_head_equals_full_head(causal):
     # the row-subset oracle (for sequences too long to form P) gives the same

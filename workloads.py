@@ -216,3 +216,31 @@ def make_decode_inputs(wl: DecodeWorkload, lengths: Optional[Sequence[int]] = No
     k = torch.randn(wl.B, wl.nk, wl.H, wl.d, generator=g).to(dt)
     v = torch.randn(wl.B, wl.nk, wl.H, wl.d, generator=g).to(dt)
     return DecodeInputs(wl, q, k, v, seq)
+
+
+def paged_cache(k: torch.Tensor, v: torch.Tensor, page_size: int, seed: int,
+                lengths: Optional[Sequence[int]] = None, spare: int = 2):
+    """The caches k, v [B, nk, H, d] laid out as a paged cache: pools
+    [num_pages, page_size, H, d] whose pages sit in a seeded random order,
+    with `spare` unused pages, and a table [B, ceil(nk / page_size)] (int32)
+    naming the pool page of each page of each sequence.  Unused pages and the
+    padding rows of a last partial page hold NaN; table entries of pages at or
+    past a sequence's length are -1 (lengths = all nk if None).  Layout only:
+    the cache contents are those of k and v."""
+    B, nk, H, d = k.shape
+    max_pages = -(-nk // page_size)
+    n = B * max_pages + spare
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(seed))
+    kp = torch.full((n, page_size, H, d), float("nan"), dtype=k.dtype)
+    vp = torch.full_like(kp, float("nan"))
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    for b in range(B):
+        L = nk if lengths is None else int(lengths[b])
+        for p in range(max_pages):
+            lo, hi = p * page_size, min((p + 1) * page_size, nk)
+            slot = int(perm[b * max_pages + p])
+            kp[slot, :hi - lo] = k[b, lo:hi]
+            vp[slot, :hi - lo] = v[b, lo:hi]
+            if lo < L:
+                table[b, p] = slot
+    return kp, vp, table
