@@ -15,6 +15,9 @@
 //     the merge kernel combines the chunks of a query with the online-softmax
 //     rule of section 3.2 of the lab write-up: M = max m, L = sum l 2^(m - M),
 //     O = sum O_chunk 2^(m - M) / L, LSE = (M + log2 L) ln 2.
+//   - A paged cache (page pools plus a block table) runs the same split
+//     kernel with each chunk's page numbers staged in LDS first; only the row
+//     addresses differ.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
