@@ -90,27 +90,77 @@ def measured_traffic(kernel: str):
     return rec.get("traffic_bytes")
 
 
-def cpu_baseline(wl, x, n_heads: int):
+def cpu_model() -> str:
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, x, n_heads: int, repeats: int = 3, warmup: int = 1):
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    n_heads (batch, head) pairs at full sequence length (0 = every pair),
-    forward + backward, OpenMP over the pairs on all host cores."""
+    n_heads (sequence, head) pairs at full length (0 = every pair), forward
+    and backward timed separately, `warmup` untimed runs then the median of
+    `repeats`; OpenMP runs one pair per host thread."""
+    import statistics
+
     import oracle
     from workloads import as_f64_tokens
     oracle.build()
-    all_pairs = [(s, h) for s in range(wl.B) for h in range(wl.H)]
-    sel = all_pairs if n_heads <= 0 or n_heads >= len(all_pairs) else all_pairs[::len(all_pairs) // n_heads][:n_heads]
+    nseq = len(x.lengths) if wl.varlen else wl.B
+    all_pairs = [(s, h) for s in range(nseq) for h in range(wl.H)]
+    if n_heads <= 0 or n_heads >= len(all_pairs):
+        sel = all_pairs
+    else:
+        sel = all_pairs[::max(1, len(all_pairs) // n_heads)][:n_heads]
     q, k, v, do = (as_f64_tokens(t) for t in (x.q, x.k, x.v, x.do))
-    t0 = time.perf_counter()
-    oracle.forward(q, k, v, scale=wl.scale, causal=wl.causal, N=wl.N, heads=sel)
-    oracle.backward(q, k, v, do, scale=wl.scale, causal=wl.causal, N=wl.N, heads=sel)
-    dt = time.perf_counter() - t0
-    per_head = (wl.N * (wl.N + 1) // 2) if wl.causal else wl.N * wl.N
-    flops = 14.0 * wl.d * per_head * len(sel)
-    what = "all" if len(sel) == len(all_pairs) else f"{len(sel)} of"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"{what} {len(all_pairs)} (batch, head) pairs of the {wl.name} workload at full length, "
-                      f"fp64 forward + backward, {flops / 1e9:.1f} GFLOP"}
+    kw = dict(scale=wl.scale, causal=wl.causal, dropout_p=wl.dropout_p, seed=wl.seed, heads=sel)
+    kw.update(lengths=x.lengths) if wl.varlen else kw.update(N=wl.N)
+    times = {"fwd": [], "bwd": []}
+    for r in range(warmup + repeats):
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, **kw)
+        t1 = time.perf_counter()
+        oracle.backward(q, k, v, do, **kw)
+        t2 = time.perf_counter()
+        if r >= warmup:
+            times["fwd"].append(t1 - t0)
+            times["bwd"].append(t2 - t1)
+    lens = x.lengths if wl.varlen else [wl.N] * wl.B
+    pairs = sum((lens[s] * (lens[s] + 1) // 2) if wl.causal else lens[s] ** 2 for s, _ in sel)
+    tf, tb = statistics.median(times["fwd"]), statistics.median(times["bwd"])
+    ff, fb = 4.0 * wl.d * pairs, 10.0 * wl.d * pairs
+    what = "every" if len(sel) == len(all_pairs) else f"{len(sel)} of the"
+    threads = min(oracle.max_threads(), len(sel))
+    return {"value": (ff + fb) / (tf + tb) / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_threads": oracle.max_threads(),
+            "fwd": {"seconds": tf, "tflops": ff / tf / 1e12, "gflop": ff / 1e9},
+            "bwd": {"seconds": tb, "tflops": fb / tb / 1e12, "gflop": fb / 1e9},
+            "seconds": tf + tb, "timing": f"{warmup} warm-up run(s), median of {repeats}",
+            "sample": f"{what} {len(all_pairs)} (sequence, head) pairs of the {wl.name} workload at full length, "
+                      f"fp64 forward and backward timed separately, {(ff + fb) / 1e9:.1f} GFLOP per run "
+                      f"(4*d and 10*d flops per visible pair)"}
+
+
+def cpu_baseline_configs(args) -> int:
+    """The oracle baseline on every workload, one JSON line each: the small
+    and headline workloads (and any listed) with 1 warm-up and the median of
+    3 over every (sequence, head) pair, the long and varlen ones in a single
+    run.  Host work only; minutes in all."""
+    import workloads
+    names = args.workload.split(",") if args.workload else list(workloads.WORKLOADS)
+    for name in names:
+        wl = workloads.WORKLOADS[name]
+        x = workloads.make_inputs(wl)
+        big = wl.N * wl.N * wl.H * wl.B > 4096 * 4096 * 32 or wl.varlen
+        rec = cpu_baseline(wl, x, 0, repeats=1 if big else 3, warmup=0 if big else 1)
+        print(json.dumps({"workload": name, "cpu_baseline": rec}), flush=True)
+    return 0
 
 
 def copy_calibration(nbytes: int, steps: int) -> int:
@@ -450,8 +500,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the causal B4 H8 N4096 d128 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32,
-                    help="oracle sample size in (batch, head) pairs (about 10-30 s of host work); 0 = all")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="oracle sample size in (sequence, head) pairs (about 10-30 s of host work); 0 = all")
+    ap.add_argument("--cpu-baseline-configs", action="store_true",
+                    help="time only the fp64 oracle on every workload (or the --workload list), one JSON line each")
     ap.add_argument("--copy-bytes", type=int, default=0, help="run only the counter calibration pass over this many bytes")
     ap.add_argument("--pmc-summary", default="", help="directory of rocprofv3 --pmc runs to turn into the traffic file")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30, help="bytes of the calibration pass of --pmc-summary")
@@ -481,6 +533,8 @@ def main() -> int:
 
     if args.copy_bytes:
         return copy_calibration(args.copy_bytes, args.steps)
+    if args.cpu_baseline_configs:
+        return cpu_baseline_configs(args)
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary, args.calib_bytes)
 
@@ -609,7 +663,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and bm is None and not wl.varlen:
+    if not args.no_cpu_baseline and bm is None:
         line["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_heads)
     print(json.dumps(line), flush=True)
     return 0

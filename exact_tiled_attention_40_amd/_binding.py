@@ -103,8 +103,9 @@ def _geometry(q, cu_seqlens, max_seqlen):
         return B, N, H, d, q.stride(1)
     if q.dim() != 3:
         raise ValueError("varlen q/k/v must be [total, H, d]")
-    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
-        raise ValueError("cu_seqlens must be an int32 device tensor")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1 \
+            or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a contiguous 1-d int32 device tensor of nseq + 1 prefix sums")
     if max_seqlen is None:
         raise ValueError("varlen needs max_seqlen")
     _, H, d = q.shape
@@ -117,6 +118,17 @@ def _same_geometry(ref, *ts):
     for t in ts:
         if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype or t.device != ref.device:
             raise ValueError("q, k, v (and dq, dk, dv) must share shape, strides, dtype and device")
+
+
+def _check_like(name, t, shape, dtype, device):
+    """t must be a contiguous tensor of the given shape, dtype and device."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)} on {device}, got {t.dtype} {tuple(t.shape)} "
+                         f"on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _block_mask(block_mask, B, H, N, device):
@@ -144,6 +156,8 @@ def fa_forward(q, k, v, *, scale=None, causal=False, cu_seqlens=None, max_seqlen
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, q.shape[:-1], torch.float32, q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
             _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1), _stream(stream), _DTYPES[q.dtype], ld)
     if block_mask is None:
@@ -189,8 +203,9 @@ def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_se
     B, N, H, d, ld = _geometry(q, cu_seqlens, max_seqlen)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if not (o.is_contiguous() and dout.is_contiguous() and lse.is_contiguous()):
-        raise ValueError("o, dout and lse must be contiguous")
+    _check_like("o", o, q.shape, q.dtype, q.device)
+    _check_like("dout", dout, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, q.shape[:-1], torch.float32, q.device)
     if dq is None and dk is None and dv is None:
         if ld != H * d:
             raise ValueError("pass dq/dk/dv explicitly for strided q/k/v")
@@ -199,6 +214,8 @@ def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_se
     need = fa_backward_workspace_size(B, N, H, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
             float(scale), int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
             _stream(stream), _DTYPES[q.dtype], ld, _ptr(workspace), workspace.numel() * workspace.element_size())

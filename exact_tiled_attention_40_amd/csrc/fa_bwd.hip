@@ -81,13 +81,7 @@ struct BwdArgs {
 };
 
 __device__ __forceinline__ void seq_range(const BwdArgs& a, int b, int& start, int& L) {
-  if (a.cu) {
-    start = a.cu[b];
-    L = a.cu[b + 1] - start;
-  } else {
-    start = b * a.N;
-    L = a.N;
-  }
+  seq_bounds(a.cu, b, a.B, a.N, start, L);
 }
 
 // ---------------------------------------------------------------- dQ (+ D)

@@ -104,13 +104,7 @@ __global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_k
   const int h = bh % a.H;
   const int qb = CAUSAL ? a.nqb - 1 - rank : rank;
   int start, L;
-  if (a.cu) {
-    start = a.cu[b];
-    L = a.cu[b + 1] - start;
-  } else {
-    start = b * a.N;
-    L = a.N;
-  }
+  seq_bounds(a.cu, b, a.B, a.N, start, L);
   const int q0 = qb * kBR;
   if (q0 >= L) return;
 

@@ -22,6 +22,32 @@ struct AttnShape {
   int nb;                  // mask blocks per side, ceil(N / 128)
 };
 
+// First token and length of sequence b of a batch of B sequences whose
+// longest is N.  Fixed length: b*N and N.  Varlen: from the prefix sums cu
+// (cu[b] .. cu[b+1] - 1 are the sequence's tokens, cu[B] tokens in all),
+// clamped so that every token index the kernels form lies in
+// [0, min(cu[B], B*N)): a sequence longer than N is cut to its first N
+// tokens (the grid and the tile lists are sized for N), and prefix sums that
+// are not monotone or exceed B*N (the rows of the backward workspace) give
+// empty or shortened sequences instead of accesses out of bounds.
+__host__ __device__ inline void seq_bounds(const int32_t* cu, int b, int B, int N, int& start, int& L) {
+  if (!cu) {
+    start = b * N;
+    L = N;
+    return;
+  }
+  const int cap = B * N;  // fits in int32: checked on the host
+  int total = cu[B];
+  total = total < 0 ? 0 : (total > cap ? cap : total);
+  int s = cu[b];
+  s = s < 0 ? 0 : (s > total ? total : s);
+  int e = cu[b + 1];
+  const int e_max = (total - s < N) ? total : s + N;
+  e = e < s ? s : (e > e_max ? e_max : e);
+  start = s;
+  L = e - s;
+}
+
 hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, const void* v, void* o,
                           float* lse, hipStream_t stream);
 

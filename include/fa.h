@@ -36,7 +36,12 @@
  *     lse is [total, H].  N must be >= every sequence length (it sizes the
  *     grid).  Causal masking and dropout indices are local to each sequence;
  *     queries never see another sequence.  Its contents are a precondition
- *     the library does not read on the host.
+ *     the library does not read on the host.  The kernels clamp them so that
+ *     no access leaves [0, min(cu_seqlens[B], B*N)) tokens: a sequence longer
+ *     than N is cut to its first N tokens (its later rows are not written),
+ *     and prefix sums that are negative, decreasing or past B*N give empty or
+ *     shortened sequences (outputs unspecified, never an out-of-bounds
+ *     access).
  *   - Causal: query i sees keys j <= i (queries and keys have equal length).
  *   - scale multiplies Q K^T before the softmax (1/sqrt(d) is the usual value).
  *   - Dropout (0 < dropout_p < 1) drops entries of the normalised P before

@@ -8,9 +8,10 @@
  *
  * What it computes follows the three-step definition of attention on the
  * page "企业官网建设流程全解析" (dpshk.com lab write-up), section 2.1
- * ("三步计算背后的显存账本"): S = Q K^T, P = row softmax(S), O = P V, with
- * the scale 1/sqrt(d) applied to S as in the einsum reference of the
- * tiemojia.cn article ("scores = einsum(bthd,bshd->bhts)/sqrt_d").  Tensors
+ * ("三步计算背后的显存账本"): S = Q K^T, P = row softmax(S), O = P V.  The
+ * scores are multiplied by the scale (1/sqrt(d) by default) before the
+ * softmax, which is how the plain einsum reference in the code-comparison
+ * section of the tiemojia.cn PyTorch article forms them.  Tensors
  * use the [batch, seq, heads, head_dim] layout named in section 4.2 of the
  * lab write-up.  Each (sequence, head) pair is computed on its own:
  *

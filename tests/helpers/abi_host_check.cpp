@@ -124,6 +124,52 @@ int main() {
                         pneed) == FA_ERR_BAD_SHAPE);
   CHECK(fa_dropout_mask(static_cast<uint8_t*>(P), 0, 0, 16, 0.25f, 1, nullptr) == FA_OK && last_thresh == 16384u);
   for (int c = 0; c <= 8; ++c) CHECK(fa_strerror(c) != nullptr && std::strlen(fa_strerror(c)) > 0);
+  // sequence bounds the kernels use: fixed length, valid prefix sums, and
+  // prefix sums that break the precondition (a sequence longer than N, not
+  // monotone, negative, past B*N) -- every token index stays inside
+  // [0, min(cu[B], B*N)) and no length exceeds N
+  {
+    int st = -1, L = -1;
+    fa::seq_bounds(nullptr, 3, 4, 7, st, L);
+    CHECK(st == 21 && L == 7);
+    const int32_t good[4] = {0, 5, 5, 12};
+    fa::seq_bounds(good, 0, 3, 8, st, L);
+    CHECK(st == 0 && L == 5);
+    fa::seq_bounds(good, 1, 3, 8, st, L);
+    CHECK(st == 5 && L == 0);
+    fa::seq_bounds(good, 2, 3, 8, st, L);
+    CHECK(st == 5 && L == 7);
+    const int32_t longer[3] = {0, 30, 33};  // first sequence longer than N = 10
+    fa::seq_bounds(longer, 0, 2, 10, st, L);
+    CHECK(st == 0 && L == 10);
+    fa::seq_bounds(longer, 1, 2, 10, st, L);
+    CHECK(st == 20 && L == 0);  // past B*N = 20 tokens
+    const int32_t backwards[4] = {0, 9, 4, 6};
+    fa::seq_bounds(backwards, 1, 3, 9, st, L);
+    CHECK(st == 6 && L == 0);
+    uint32_t rng = 12345u;
+    auto next = [&rng](int lo, int hi) {
+      rng = rng * 1664525u + 1013904223u;
+      return lo + (int)((rng >> 8) % (uint32_t)(hi - lo + 1));
+    };
+    for (int trial = 0; trial < 20000; ++trial) {
+      const int B = next(1, 6), N = next(1, 40);
+      int32_t cu[7];
+      for (int i = 0; i <= B; ++i) cu[i] = next(-60, 300);
+      if (trial % 3 == 0) {  // mostly valid ones too
+        cu[0] = 0;
+        for (int i = 1; i <= B; ++i) cu[i] = cu[i - 1] + next(0, N + 3);
+      }
+      const int total = cu[B] < 0 ? 0 : (cu[B] > B * N ? B * N : cu[B]);
+      for (int b = 0; b < B; ++b) {
+        fa::seq_bounds(cu, b, B, N, st, L);
+        CHECK(st >= 0 && L >= 0 && L <= N && st + L <= total);
+        if (cu[0] == 0 && cu[b] >= 0 && cu[b + 1] - cu[b] <= N && cu[b + 1] >= cu[b] && cu[B] <= B * N &&
+            cu[b + 1] <= cu[B])
+          CHECK(st == cu[b] && L == cu[b + 1] - cu[b]);  // a valid sequence is left as it is
+      }
+    }
+  }
   std::printf("abi host check: clean (%d launches)\n", calls);
   return 0;
 }

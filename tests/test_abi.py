@@ -240,3 +240,32 @@ def test_abi_front_end_under_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0"))
     assert r.returncode == 0, r.stdout + r.stderr
     assert "clean" in r.stdout
+
+
+# ------------------------------------------------------------ binding checks
+
+def test_binding_rejects_mismatched_outputs_before_the_library():
+    # the binding checks every caller-given output and auxiliary tensor before
+    # a pointer reaches the library (CPU tensors here: a call that passed
+    # the checks would need a GPU, so only rejections are exercised)
+    import torch
+    import exact_tiled_attention_40_amd as fa
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    bad_out = [torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16), torch.zeros(1, 8, 2, 64, dtype=torch.float16),
+               torch.zeros(1, 8, 64, 2, dtype=torch.bfloat16).transpose(2, 3)]
+    for out in bad_out:
+        with pytest.raises(ValueError):
+            fa.fa_forward(q, q, q, out=out)
+    for lse in (torch.zeros(1, 8, 2, dtype=torch.float16), torch.zeros(1, 8, 3), torch.zeros(1, 2, 8).transpose(1, 2)):
+        with pytest.raises(ValueError):
+            fa.fa_forward(q, q, q, out=torch.zeros_like(q), lse=lse)
+    lse = torch.zeros(1, 8, 2)
+    for o, dout, l in ((q[..., :32], q, lse), (q, q.float(), lse), (q, q, lse.double()), (q, q, lse[:, :4])):
+        with pytest.raises(ValueError):
+            fa.fa_backward(q, q, q, o, l, dout)
+    with pytest.raises(ValueError):
+        fa.fa_backward(q, q, q, q, lse, q, workspace=torch.zeros(64, dtype=torch.uint8)[::2])
+    qv = torch.zeros(20, 2, 64, dtype=torch.bfloat16)
+    for cu in (torch.tensor([0, 20], dtype=torch.int64), torch.tensor([0, 20], dtype=torch.int32)):
+        with pytest.raises(ValueError):  # int64, or not on the device
+            fa.fa_forward(qv, qv, qv, cu_seqlens=cu, max_seqlen=20)

@@ -35,3 +35,20 @@ def test_clock_reader_parses_current_level(tmp_path):
     c.samples = [300, 900, 2000, 1900, 2100, 2050]   # ramping up from idle, then settled
     s = c.summary()
     assert (s["median"], s["min"], s["max"], s["samples"]) == (2050, 1900, 2100, 3)
+
+
+def test_cpu_baseline_reports_forward_and_backward():
+    wl = workloads.WORKLOADS["tiny_B1_H2_N128_d64_f16"]
+    x = workloads.make_inputs(wl)
+    r = bench.cpu_baseline(wl, x, 0, repeats=3, warmup=1)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] == min(2, r["host_threads"])
+    pairs = 2 * 128 * 128
+    assert abs(r["fwd"]["gflop"] - 4 * 64 * pairs / 1e9) < 1e-12
+    assert abs(r["bwd"]["gflop"] - 10 * 64 * pairs / 1e9) < 1e-12
+    assert r["fwd"]["seconds"] > 0 and r["bwd"]["seconds"] > 0
+    assert abs(r["value"] - 14 * 64 * pairs / (r["fwd"]["seconds"] + r["bwd"]["seconds"]) / 1e12) < 1e-9
+    assert r["cpu_model"] and "median of 3" in r["timing"]
+    # a varlen workload's pairs follow its drawn lengths (one short sequence here)
+    wlv = workloads.custom(0, 2, 0, 64, "f16", True, lengths=[5, 17], dropout_p=0.1, seed=3)
+    rv = bench.cpu_baseline(wlv.wl, wlv, 0, repeats=1, warmup=0)
+    assert abs(rv["fwd"]["gflop"] - 4 * 64 * 2 * (15 + 153) / 1e9) < 1e-12

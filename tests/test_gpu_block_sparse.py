@@ -52,9 +52,9 @@ def check(x, bm):
     pairs = [(s, h) for s in range(nseq) for h in range(x.wl.H)]
     for name, g, r in zip(("dQ", "dK", "dV"), grads, g_ref):
         assert torch.isfinite(g.float()).all(), name
-        e, worst = rel_fro(x, g, r, pairs, floor_ref=g_ref[2])
+        e, worst, over = rel_fro(x, g, r, pairs, floor_ref=g_ref[2])
         print(f"[{x.wl.name}] {name} rel Frobenius {e:.3e} (worst head {worst:.3e})", flush=True)
-        assert e <= GRAD_TOL, (name, e)
+        assert e <= GRAD_TOL and not over, (name, e, over)
     # structural zeros: dQ of rows that see no key, dK and dV of keys that no
     # query sees
     dq, dk, dv = (tokens_f64(g) for g in grads)

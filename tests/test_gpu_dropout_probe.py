@@ -1,22 +1,36 @@
 """Dropout keep bits recovered bit for bit through the fused kernels (needs
 an MI355X).
 
-With Q = K = 0 every visible score is 0, so P is uniform, 1/n_i over the n_i
-keys query i sees.  Forward: with one-hot V rows (v_j = e_{j-o} for
-o <= j < o + d, else 0), O[i][c] = keep(i, o + c) / (n_i (1 - p)) for a
-visible key o + c and 0 otherwise, so O[i][c] != 0 exactly when the forward
-kernel kept element (i, o + c).  Key-side backward: with one-hot dO rows
-(dO_i = e_{i-o} for o <= i < o + d), dV_j = sum_i Z_ij dO_i gives
-dV_j[c] = keep(o + c, j) / (n_{o+c} (1 - p)) for a visible pair, so the key
-side's keep bits are read off dV the same way.  Sliding o over the sequence
-covers every (query, key) pair; the bits must equal the oracle's keep mask
-(Philox-4x32-10 as the header defines it) everywhere a pair is visible.
+With Q = 0 every visible score is 0, so P is uniform, 1/n_i over the n_i
+keys query i sees (n_i = i + 1 causal, L otherwise).
+
+Forward: with K = 0 and one-hot V rows (v_j = e_{j-o} for o <= j < o + d,
+else 0), O[i][c] = keep(i, o + c) / (n_i (1 - p)) for a visible key o + c,
+so O[i][c] != 0 exactly when the forward kernel kept element (i, o + c).
+
+Key-side backward: with one-hot dO rows (dO_i = e_{i-o} for o <= i < o + d),
+dV_j = sum_i Z_ij dO_i gives dV_j[c] = keep(o + c, j) / (n_{o+c} (1 - p)), so
+the key-side kernel's bits are read off dV the same way.
+
+Query-side backward: with one-hot K rows (k_j = e_{j-o}), every V row and
+every dO row e_0, dP_ij = dO_i . v_j = 1 and dQ_i[c] = scale dS_{i,o+c}
+with dS_ij = (keep_ij / (1 - p) - D_i) / n_i, D_i = dO_i . O_i = O_i[0].
+A kept element gives dS above, a dropped one below
+(0.5 / (1 - p) - D_i) / n_i, half a step of 1 / (n_i (1 - p)) on either
+side, so the query-side kernel's bits are read off dQ against that
+threshold (D_i taken from the forward's own O).
+
+Sliding o over the sequence covers every (query, key) pair; the bits must
+equal the oracle's keep mask (Philox-4x32-10 as the oracle header defines
+it) wherever a pair is visible, and invisible pairs must contribute exactly
+nothing.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import workloads
 from conftest import gpu_available
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -24,11 +38,28 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="n
 DT = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
-def probe(lengths, H, d, dtype, causal, p, seed, varlen):
-    """Keep bits [seq][h] (L x L, -1 where not visible) seen by the forward
-    and by the key-side backward."""
+def _onehot_rows(T, H, d, starts, lengths, o, dtype, dev):
+    """[T, H, d] with row starts[s] + o + c of every sequence = e_c (c < d)."""
+    x = torch.zeros(T, H, d, dtype=dtype, device=dev)
+    rows, cols = [], []
+    for st, L in zip(starts, lengths):
+        w = max(0, min(d, L - o))
+        rows.append(torch.arange(w) + int(st) + o)
+        cols.append(torch.arange(w))
+    if rows:
+        r = torch.cat(rows).to(dev)
+        c = torch.cat(cols).to(dev)
+        x[r, :, c] = 1
+    return x
+
+
+def probe(lengths, H, d, dtype, causal, p, seed, varlen, heads=None):
+    """Keep bits [seq][head] (L x L, -1 where not read) seen by the forward,
+    the key-side backward and the query-side backward, for the given heads
+    (all if None)."""
     import exact_tiled_attention_40_amd as fa
     dev = torch.device("cuda")
+    heads = list(range(H)) if heads is None else list(heads)
     nseq, N = len(lengths), max(lengths)
     T = sum(lengths) if varlen else nseq * N
     starts = np.cumsum([0] + list(lengths))[:-1] if varlen else [s * N for s in range(nseq)]
@@ -37,31 +68,60 @@ def probe(lengths, H, d, dtype, causal, p, seed, varlen):
         cu = torch.tensor(np.cumsum([0] + list(lengths)), dtype=torch.int32, device=dev)
         kw.update(cu_seqlens=cu, max_seqlen=N)
     shape = (T, H, d) if varlen else (nseq, N, H, d)
-    q = torch.zeros(shape, dtype=DT[dtype], device=dev)
-    k = torch.zeros_like(q)
-    fwd_bits = [[np.full((L, L), -1, np.int8) for _ in range(H)] for L in lengths]
-    bwd_bits = [[np.full((L, L), -1, np.int8) for _ in range(H)] for L in lengths]
+    dt = DT[dtype]
+    scale = 1.0 / np.sqrt(d)
+    zero = torch.zeros(shape, dtype=dt, device=dev)
+    e0 = torch.zeros(T, H, d, dtype=dt, device=dev)
+    e0[:, :, 0] = 1
+    e0 = e0.reshape(shape)
+    hsel = torch.tensor(heads, device=dev)
+    bits = {kind: [[np.full((L, L), -1, np.int8) for _ in heads] for L in lengths] for kind in ("fwd", "kv", "q")}
     for o in range(0, N, d):
-        onehot = torch.zeros(T, H, d, dtype=torch.float32)
-        for s, L in enumerate(lengths):
-            for c in range(min(d, L - o) if L > o else 0):
-                onehot[starts[s] + o + c, :, c] = 1.0
-        x = onehot.to(DT[dtype]).to(dev).reshape(shape)
-        out, lse = fa.fa_forward(q, k, x, **kw)
-        dq, dk, dv = fa.fa_backward(q, k, x, out, lse, x, **kw)
+        x = _onehot_rows(T, H, d, starts, lengths, o, dt, dev).reshape(shape)
+        # forward (one-hot V) and key side (one-hot dO)
+        out, lse = fa.fa_forward(zero, zero, x, **kw)
+        _, _, dv = fa.fa_backward(zero, zero, x, out, lse, x, **kw)
+        # query side: one-hot K, V = dO = e_0
+        out0, lse0 = fa.fa_forward(zero, x, e0, scale=scale, **kw)
+        dq, _, _ = fa.fa_backward(zero, x, e0, out0, lse0, e0, scale=scale, **kw)
         torch.cuda.synchronize()
-        out = out.reshape(T, H, d).float().cpu().numpy()
-        dv = dv.reshape(T, H, d).float().cpu().numpy()
+        out = out.reshape(T, H, d)[:, hsel].float().cpu().numpy()
+        dv = dv.reshape(T, H, d)[:, hsel].float().cpu().numpy()
+        dq = dq.reshape(T, H, d)[:, hsel].float().cpu().numpy()
+        dd = out0.reshape(T, H, d)[:, hsel, 0].float().cpu().numpy()
         for s, L in enumerate(lengths):
             if L <= o:
                 continue
             w = min(d, L - o)
-            rows = out[starts[s]:starts[s] + L]        # [L, H, d]: O[i][c] <-> (i, o + c)
-            keys = dv[starts[s]:starts[s] + L]         # [L, H, d]: dV[j][c] <-> (o + c, j)
-            for h in range(H):
-                fwd_bits[s][h][:, o:o + w] = rows[:, h, :w] != 0
-                bwd_bits[s][h][o:o + w, :] = (keys[:, h, :w] != 0).T
-    return fwd_bits, bwd_bits
+            sl = slice(starts[s], starts[s] + L)
+            n = (np.arange(L) + 1 if causal else np.full(L, L)).astype(np.float64)
+            for t in range(len(heads)):
+                bits["fwd"][s][t][:, o:o + w] = out[sl, t, :w] != 0
+                bits["kv"][s][t][o:o + w, :] = (dv[sl, t, :w] != 0).T
+                thr = scale * (0.5 / (1.0 - np.float32(p)) - dd[sl, t]) / n
+                got = dq[sl, t, :w]
+                vis = (np.arange(w)[None, :] + o <= np.arange(L)[:, None]) if causal else np.ones((L, w), bool)
+                b = np.where(vis, got > thr[:, None], got != 0).astype(np.int8)
+                bits["q"][s][t][:, o:o + w] = b
+    return heads, bits
+
+
+def check_probe(lengths, H, d, dtype, causal, p, seed, varlen, heads=None):
+    heads, bits = probe(lengths, H, d, dtype, causal, p, seed, varlen, heads)
+    for s, L in enumerate(lengths):
+        vis = np.tril(np.ones((L, L), bool)) if causal else np.ones((L, L), bool)
+        for t, h in enumerate(heads):
+            ref = oracle.keep_mask(seed, p, s, h, L).astype(bool)
+            counts = {}
+            for kind in ("fwd", "kv", "q"):
+                b = bits[kind][s][t]
+                assert (b >= 0).all(), (kind, s, h)
+                counts[kind] = int((b[vis].astype(bool) != ref[vis]).sum())
+                # invisible pairs contribute nothing
+                assert not b[~vis].any(), (kind, s, h)
+            print(f"[seq {s} head {h} L={L}] mismatches: forward {counts['fwd']}, key side {counts['kv']}, "
+                  f"query side {counts['q']}; kept {ref[vis].mean():.4f}", flush=True)
+            assert counts == {"fwd": 0, "kv": 0, "q": 0}, counts
 
 
 @pytest.mark.parametrize("lengths,H,d,dtype,causal,p,seed,varlen", [
@@ -69,19 +129,17 @@ def probe(lengths, H, d, dtype, causal, p, seed, varlen):
     ([200], 3, 64, "f16", False, 0.5, 1005, False),
     ([5, 130, 77, 260], 2, 128, "bf16", True, 0.1, 99, True),
     ([70, 33], 1, 32, "f16", False, 0.25, 7, True),
+    ([150, 90], 2, 96, "bf16", True, 0.2, 12345, True),
 ])
 def test_keep_bits_through_fused_kernels(lengths, H, d, dtype, causal, p, seed, varlen):
-    fwd_bits, bwd_bits = probe(lengths, H, d, dtype, causal, p, seed, varlen)
-    for s, L in enumerate(lengths):
-        vis = np.tril(np.ones((L, L), bool)) if causal else np.ones((L, L), bool)
-        for h in range(len(fwd_bits[s])):
-            ref = oracle.keep_mask(seed, p, s, h, L).astype(bool)
-            f, b = fwd_bits[s][h], bwd_bits[s][h]
-            assert (f[vis] >= 0).all() and (b[vis] >= 0).all()
-            nf = int((f[vis].astype(bool) != ref[vis]).sum())
-            nb = int((b[vis].astype(bool) != ref[vis]).sum())
-            print(f"[seq {s} head {h} L={L}] forward mismatches {nf}, key-side mismatches {nb}, "
-                  f"kept {ref[vis].mean():.3f}", flush=True)
-            assert nf == 0 and nb == 0
-            # masked-out pairs contribute nothing
-            assert not f[~vis].any() and not b[~vis].any()
+    check_probe(lengths, H, d, dtype, causal, p, seed, varlen)
+
+
+def test_keep_bits_varlen_workload_shape():
+    """The varlen dropout workload's own shape: its 16 drawn sequence lengths
+    (up to 4096 tokens, packed), H = 32, d = 128, bf16, causal, p = 0.1, its
+    seed; heads 0 and 31 of every sequence, sequence 15 included."""
+    wl = workloads.WORKLOADS["varlen16_H32_d128_bf16_causal_p0.1"]
+    lengths = workloads.make_inputs(wl, with_do=False).lengths
+    print(f"[varlen workload shape] lengths {lengths}", flush=True)
+    check_probe(lengths, wl.H, wl.d, wl.dtype, wl.causal, wl.dropout_p, wl.seed, True, heads=[0, 31])

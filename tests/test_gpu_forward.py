@@ -114,12 +114,3 @@ def test_dropout_mask_bit_exact():
         m = fa.fa_dropout_mask(b, h, N, p, seed).cpu().numpy()
         ref = oracle.keep_mask(seed, p, b, h, N)
         assert np.array_equal(m, ref), (b, h, N)
-
-
-@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
-def test_forward_workload(name):
-    x = workloads.make_inputs(workloads.WORKLOADS[name], with_do=False)
-    n_heads = {"tiny_B1_H2_N128_d64_f16": None, "packed_qkv_B2_H12_N2048_d64_f16": 6,
-               "causal_B4_H8_N4096_d128_bf16": 3, "long_causal_B1_H16_N8192_d128_bf16_kx4": 3,
-               "varlen16_H32_d128_bf16_causal_p0.1": 3}[name]
-    check(x, n_heads)

@@ -138,6 +138,12 @@ def custom(B: int, H: int, N: int, d: int, dtype: str = "bf16", causal: bool = F
     return make_inputs(wl)
 
 
+def ragged_lengths(n: int, lo: int, hi: int, seed: int) -> list:
+    """n sequence lengths, discrete uniform on [lo, hi] (numpy generator)."""
+    import numpy as np
+    return [int(x) for x in np.random.default_rng(seed).integers(lo, hi + 1, n)]
+
+
 def as_f64_tokens(x: torch.Tensor):
     """[B, N, H, d] or [T, H, d] (any strides) -> contiguous float64 numpy [tokens, H, d]."""
     x = x.detach().to("cpu")
