@@ -22,6 +22,7 @@ FA_DTYPE_BF16 = 1
 FA_MASK_BLOCK = 128       # rows and columns of one block-mask entry
 FA_MASK_MAX_N = 65536     # longest sequence the block-sparse calls accept
 FA_DECODE_MAX_Q = 8       # new query tokens per sequence in one decode step
+FA_NOALLOC_MAX_ROWS = 1 << 22  # B*N*H limit of fa_backward_noalloc
 _DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 
 
@@ -45,6 +46,8 @@ def _load():
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, vp, i, i64,
                                 vp, ctypes.c_size_t]
     lib.fa_backward.restype = i
+    lib.fa_backward_noalloc.argtypes = lib.fa_backward.argtypes[:-2]
+    lib.fa_backward_noalloc.restype = i
     lib.fa_backward_stage.argtypes = [i] + lib.fa_backward.argtypes
     lib.fa_backward_stage.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
@@ -229,6 +232,28 @@ def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_se
         _check(_lib.fa_backward(*args))
     else:
         _check(_lib.fa_backward_stage(stage, *args))
+    return dq, dk, dv
+
+
+def fa_backward_noalloc(q, k, v, o, lse, dout, *, dq, dk, dv, scale=None, causal=False, cu_seqlens=None,
+                        max_seqlen=None, dropout_p=0.0, seed=0, stream=None):
+    """fa_backward without a workspace: the library's fixed per-GPU scratch
+    holds the backward's row arrays (B*N*H <= FA_NOALLOC_MAX_ROWS), so
+    neither this call nor the library allocates; the caller passes dq, dk,
+    dv.  Calls that overlap on one GPU race."""
+    _same_geometry(q, k, v)
+    if q.dtype not in _DTYPES:
+        raise FAError(3, fa_strerror(3))
+    B, N, H, d, ld = _geometry(q, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_like("o", o, q.shape, q.dtype, q.device)
+    _check_like("dout", dout, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, q.shape[:-1], torch.float32, q.device)
+    _same_geometry(q, dq, dk, dv)
+    _check(_lib.fa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(cu_seqlens),
+                                    float(dropout_p), int(seed) & (2**64 - 1), _stream(stream), _DTYPES[q.dtype], ld))
     return dq, dk, dv
 
 

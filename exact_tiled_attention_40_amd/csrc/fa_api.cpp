@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_internal.h"
 
@@ -98,28 +99,47 @@ size_t fa_backward_workspace_size(int B, int N, int H, int d) {
   return (size_t)(2 * ((rows * 4 + 255) & ~(uint64_t)255));
 }
 
+// Checks of the backward's tensors and sizes (everything but the workspace).
+static int check_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                          int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, int dtype,
+                          int64_t ld_qkv, const uint8_t* block_mask, bool sparse, fa::AttnShape* s) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+  int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, s);
+  if (rc != FA_OK) return rc;
+  if (sparse && (rc = check_block_mask(block_mask, N, s)) != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGNMENT;
+  return FA_OK;
+}
+
+// Enqueues the backward with its two row arrays carved from `workspace`
+// (D first, then lse * log2(e) at the next 256-byte boundary).
+static int launch_backward_ws(const fa::AttnShape& s, int stages, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              void* workspace, void* stream) {
+  float* delta = static_cast<float*>(workspace);
+  const uint64_t rows = (uint64_t)s.B * (uint64_t)s.N * (uint64_t)s.H;
+  float* lse2 = delta + ((rows * 4 + 255) & ~(uint64_t)255) / 4;
+  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, delta, lse2, stages,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 static int backward_impl(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                          int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
                          int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes,
                          const uint8_t* block_mask, bool sparse) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
   fa::AttnShape s;
-  int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
+  const int rc = check_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens, dropout_p,
+                                seed, dtype, ld_qkv, block_mask, sparse, &s);
   if (rc != FA_OK) return rc;
-  if (sparse && (rc = check_block_mask(block_mask, N, &s)) != FA_OK) return rc;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_ALIGNMENT;
   const size_t need = fa_backward_workspace_size(B, N, H, d);
   if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGNMENT;
-  float* delta = static_cast<float*>(workspace);
-  const uint64_t rows = (uint64_t)B * (uint64_t)N * (uint64_t)H;
-  float* lse2 = delta + ((rows * 4 + 255) & ~(uint64_t)255) / 4;
-  const hipError_t e = fa::launch_backward(s, q, k, v, o, lse, dout, dq, dk, dv, delta, lse2, stages,
-                                           static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launch_backward_ws(s, stages, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -156,6 +176,54 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
   if (stage < 0 || stage > 1) return FA_ERR_BAD_ARGUMENT;
   return backward_impl(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
                        dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, block_mask, true);
+}
+
+// ---------------------------------------------------- no-allocation backward
+// The backward's workspace (D and lse * log2(e), fp32 [B*N, H] each) for
+// callers that cannot allocate: a fixed array in device memory, one copy per
+// GPU, held from the first call on that GPU until the process ends.  Host
+// code only ever uses the address hipGetSymbolAddress returns for the GPU
+// (the array's name is a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+static_assert(FA_NOALLOC_SCRATCH_BYTES == 2 * (size_t)FA_NOALLOC_MAX_ROWS * 4,
+              "two fp32 arrays of FA_NOALLOC_MAX_ROWS rows, each a multiple of 256 bytes");
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[FA_NOALLOC_MAX_DEVICES];
+
+// Device address of `scratch` on the stream's GPU (the current GPU for the
+// null stream), looked up once per GPU with that GPU current.
+static int scratch_for_stream(void* stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_HIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= FA_NOALLOC_MAX_DEVICES) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return FA_ERR_HIP;
+    if (e != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                        int dtype, int64_t ld_qkv) {
+  fa::AttnShape s;
+  int rc = check_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens, dropout_p, seed,
+                          dtype, ld_qkv, nullptr, false, &s);
+  if (rc != FA_OK) return rc;
+  if ((uint64_t)B * (uint64_t)N * (uint64_t)H > (uint64_t)FA_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if ((rc = scratch_for_stream(stream, &ws)) != FA_OK) return rc;
+  return launch_backward_ws(s, fa::kBwdAll, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
 }
 
 size_t fa_decode_workspace_size(int B, int H, int nq, int nk_max, int d) {
@@ -238,6 +306,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIGNMENT: return "pointers must be 16-byte aligned, ld_qkv a multiple of 8 and >= H*d";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
     case FA_ERR_HIP: return "a HIP kernel launch failed";
+    case FA_ERR_SCRATCH_LIMIT: return "B*N*H exceeds FA_NOALLOC_MAX_ROWS, the fixed scratch of fa_backward_noalloc";
     default: return "unknown fa status code";
   }
 }

@@ -94,7 +94,8 @@ enum fa_status {
     FA_ERR_BAD_ARGUMENT = 4,   /* scale not finite, dropout_p not in [0, 1) */
     FA_ERR_ALIGNMENT = 5,      /* pointer not 16-byte aligned or bad ld_qkv */
     FA_ERR_WORKSPACE = 6,      /* workspace NULL or smaller than required */
-    FA_ERR_HIP = 7             /* a HIP launch reported an error */
+    FA_ERR_HIP = 7,            /* a HIP launch reported an error */
+    FA_ERR_SCRATCH_LIMIT = 8   /* fa_backward_noalloc: B*N*H above FA_NOALLOC_MAX_ROWS */
 };
 
 /* Forward pass.
@@ -146,6 +147,29 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       int B, int H, int N, int d, float scale, int causal,
                       const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
                       int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes);
+
+/* The backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * fa_backward without the workspace arguments.  Its two row arrays live in a
+ * fixed array of FA_NOALLOC_SCRATCH_BYTES (32 MiB) in device memory, one per
+ * GPU, which the library holds from the first call on a GPU until the
+ * process ends; the call itself allocates and frees nothing.
+ *   Arguments, layout and errors as fa_backward, plus FA_ERR_SCRATCH_LIMIT
+ *   when B*N*H > FA_NOALLOC_MAX_ROWS (checked before any HIP call).
+ *   The GPU is the stream's (the current GPU for the null stream);
+ *   FA_ERR_UNSUPPORTED for a device ordinal >= FA_NOALLOC_MAX_DEVICES.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  Nothing needs clearing between calls: each call writes every row
+ * its own kernels read. */
+#define FA_NOALLOC_MAX_ROWS (1 << 22)
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)2 * FA_NOALLOC_MAX_ROWS * 4)
+#define FA_NOALLOC_MAX_DEVICES 64
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                        int dtype, int64_t ld_qkv);
 
 /* ---------------------------------------------------------- block-sparse
  * Block-sparse attention: the block-sparse mode the coreui.cn

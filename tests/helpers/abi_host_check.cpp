@@ -101,6 +101,22 @@ int main() {
   CHECK(fa_backward_stage(1, P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0, P,
                           need) == FA_OK);
   CHECK(last_stages == 2);
+  // no-allocation backward: every argument check, then the scratch limit,
+  // all before any HIP call (a valid call needs a GPU and is not made here)
+  const int launches = calls;
+  CHECK(fa_backward_noalloc(nullptr, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1,
+                            0) == FA_ERR_NULL_POINTER);
+  CHECK(fa_backward_noalloc(P, P, P, P, F, P, P, P, P, 2, 3, 100, 80, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0) ==
+        FA_ERR_UNSUPPORTED);
+  CHECK(fa_backward_noalloc(P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 1.5f, 0, nullptr, 1, 0) ==
+        FA_ERR_BAD_ARGUMENT);
+  // B*N*H = FA_NOALLOC_MAX_ROWS + 1 is rejected; the limit itself is not
+  CHECK(fa_backward_noalloc(P, P, P, P, F, P, P, P, P, 1, 1, FA_NOALLOC_MAX_ROWS + 1, 64, 1.f, 1, nullptr, 0.f, 0,
+                            nullptr, 1, 0) == FA_ERR_SCRATCH_LIMIT);
+  CHECK(fa_backward_noalloc(P, P, P, P, F, P, P, P, P, 4, 32, 32769, 128, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0) ==
+        FA_ERR_SCRATCH_LIMIT);
+  CHECK(calls == launches);
+  CHECK(fa_backward_workspace_size(1, FA_NOALLOC_MAX_ROWS, 1, 64) == FA_NOALLOC_SCRATCH_BYTES);
   // decode and the dropout-mask export
   const size_t dneed = fa_decode_workspace_size(2, 4, 1, 3000, 128);
   CHECK(dneed > 0);
@@ -123,7 +139,7 @@ int main() {
   CHECK(fa_decode_paged(P, P, P, tbl + 0, nullptr, P, F, 2, 4, 3, 100, 1 << 30, 4, 128, 0.1f, 1, nullptr, 1, P,
                         pneed) == FA_ERR_BAD_SHAPE);
   CHECK(fa_dropout_mask(static_cast<uint8_t*>(P), 0, 0, 16, 0.25f, 1, nullptr) == FA_OK && last_thresh == 16384u);
-  for (int c = 0; c <= 8; ++c) CHECK(fa_strerror(c) != nullptr && std::strlen(fa_strerror(c)) > 0);
+  for (int c = 0; c <= 9; ++c) CHECK(fa_strerror(c) != nullptr && std::strlen(fa_strerror(c)) > 0);
   // sequence bounds the kernels use: fixed length, valid prefix sums, and
   // prefix sums that break the precondition (a sequence longer than N, not
   // monotone, negative, past B*N) -- every token index stays inside

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage", "fa_backward_stage",
+        "fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage", "fa_backward_noalloc",
+        "fa_backward_stage",
         "fa_backward_workspace_size", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size", "fa_dropout_mask",
         "fa_forward", "fa_forward_block_sparse", "fa_strerror"])
 
@@ -128,8 +129,8 @@ def test_dropout_mask_checks(lib):
 
 
 def test_strerror_covers_every_code(lib):
-    msgs = [lib.fa_strerror(c).decode() for c in range(8)]
-    assert len(set(msgs)) == 8
+    msgs = [lib.fa_strerror(c).decode() for c in range(9)]
+    assert len(set(msgs)) == 9
     assert lib.fa_strerror(99).decode().startswith("unknown")
 
 
@@ -269,3 +270,18 @@ def test_binding_rejects_mismatched_outputs_before_the_library():
     for cu in (torch.tensor([0, 20], dtype=torch.int64), torch.tensor([0, 20], dtype=torch.int32)):
         with pytest.raises(ValueError):  # int64, or not on the device
             fa.fa_forward(qv, qv, qv, cu_seqlens=cu, max_seqlen=20)
+
+
+def test_noalloc_backward_rejects_before_any_hip_call(lib):
+    vp, i, f, i64, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_uint64
+    lib.fa_backward_noalloc.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp, f, u64, vp, i, i64]
+
+    def call(B=1, H=1, N=128, d=64, p=0.0, first=P):
+        return lib.fa_backward_noalloc(first, P, P, P, P, P, P, P, P, B, H, N, d, 0.125, 1, None, p, 0, None, 1, 0)
+
+    max_rows = 1 << 22
+    assert call(N=max_rows + 1) == 8                  # FA_ERR_SCRATCH_LIMIT
+    assert call(B=4, H=32, N=32769, d=128) == 8
+    assert call(first=None) == 1 and call(d=80) == 3 and call(p=1.0) == 4
+    assert "FA_NOALLOC_MAX_ROWS" in lib.fa_strerror(8).decode()
+    assert lib.fa_backward_workspace_size(1, max_rows, 1, 64) == 2 * 4 * max_rows   # the scratch holds the limit
