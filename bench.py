@@ -516,7 +516,7 @@ def main() -> int:
                     help="with --decode: time fa_decode_paged on the same caches split into pages of this many "
                          "tokens (a power of two) in shuffled order")
     ap.add_argument("--head-dim", type=int, default=0,
-                    help="run the chosen workload with this head size instead (32, 64, 96 or 128)")
+                    help="run the chosen workload with this head size instead (32, 64, 96, 128, 160, 192 or 256)")
     ap.add_argument("--settle-s", type=float, default=1.5,
                     help="repeat the warm-up steps until this many seconds have passed (clock settling)")
     ap.add_argument("--compare-standard", action="store_true",

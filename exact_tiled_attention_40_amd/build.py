@@ -24,6 +24,10 @@ ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # fully unroll the kernels' operand-pipeline loops at every head size
+         # (at 256 with dropout the default threshold leaves some rolled, and
+         # their register arrays then live in scratch memory)
+         "-mllvm", "-pragma-unroll-threshold=1000000",
          "-I" + os.path.join(ROOT, "include")]
 
 

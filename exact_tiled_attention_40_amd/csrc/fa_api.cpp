@@ -17,7 +17,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_common(int B, int H, int N, int d, float scale, float dropout_p, int dtype, int64_t ld_qkv,
                  const int32_t* cu_seqlens, int causal, uint64_t seed, fa::AttnShape* s) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
-  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 160 && d != 192 && d != 256) return FA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_BAD_SHAPE;
   // all token offsets must fit in 32-bit signed ints (B*N tokens) and byte
   // offsets in 64 bits
@@ -301,7 +301,7 @@ const char* fa_strerror(int code) {
     case FA_OK: return "success";
     case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "B, H and N must be >= 1 (and B*N tokens must fit in int32)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dim (32, 64, 96 or 128), dtype (fp16 or bf16) or block-sparse length";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim (32, 64, 96, 128, 160, 192 or 256), dtype (fp16 or bf16) or block-sparse length";
     case FA_ERR_BAD_ARGUMENT: return "scale must be finite and > 0, dropout_p in [0, 1)";
     case FA_ERR_ALIGNMENT: return "pointers must be 16-byte aligned, ld_qkv a multiple of 8 and >= H*d";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";

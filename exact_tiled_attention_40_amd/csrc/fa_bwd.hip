@@ -44,11 +44,15 @@ namespace {
 
 constexpr int kWaves = 4;          // dK/dV kernel: one wave per SIMD
 constexpr int kThreads = 64 * kWaves;
-// dQ kernel: dense, eight waves (two per SIMD, one workgroup per CU), so
-// each K/V tile in LDS serves 256 queries; block-sparse, four waves (128
-// queries, one mask row, so the tile list is exact) and two workgroups per CU.
-template <bool SPARSE> constexpr int dq_waves() { return SPARSE ? 4 : 8; }
-template <bool SPARSE> constexpr int dq_rows() { return 32 * dq_waves<SPARSE>(); }
+// dQ kernel: dense with heads up to 128, eight waves (two per SIMD, one
+// workgroup per CU), so each K/V tile in LDS serves 256 queries;
+// block-sparse, four waves (128 queries, one mask row, so the tile list is
+// exact) and two workgroups per CU; heads above 128, four waves with one
+// workgroup per CU (the Q, dO fragments and the dQ accumulator of a wave
+// need more than half the register file).
+template <bool SPARSE, int D> constexpr int dq_waves() { return (SPARSE || D > 128) ? 4 : 8; }
+template <bool SPARSE, int D> constexpr int dq_rows() { return 32 * dq_waves<SPARSE, D>(); }
+template <bool SPARSE, int D> constexpr int dq_wgs_per_cu() { return (SPARSE && D <= 128) ? 2 : 1; }
 constexpr int kBC = 64;            // keys per tile of the dQ kernel
 constexpr int kBKV = 32 * kWaves;  // keys per dK/dV workgroup
 constexpr int kBR = 64;            // queries per tile of the dK/dV kernel
@@ -86,10 +90,11 @@ __device__ __forceinline__ void seq_range(const BwdArgs& a, int b, int& start, i
 
 // ---------------------------------------------------------------- dQ (+ D)
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
-__global__ __launch_bounds__(64 * dq_waves<SPARSE>(), SPARSE ? 2 : 1) void fa_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__((64 * dq_waves<SPARSE, D>()), (dq_wgs_per_cu<SPARSE, D>())) void fa_bwd_dq_kernel(
+    BwdArgs a) {
   using T = MTile<D, kBC>;
-  constexpr int kWavesQ = dq_waves<SPARSE>();
-  constexpr int kBQ = dq_rows<SPARSE>();
+  constexpr int kWavesQ = dq_waves<SPARSE, D>();
+  constexpr int kBQ = dq_rows<SPARSE, D>();
   constexpr int kNS = 2 * (D / 16);  // S^T and dP^T products per 32-key half (D/16 k-steps each)
   constexpr int kNQ = 2 * (D / 32);  // dQ^T products per 32-key half (two 16-key slices x D/32 tiles)
   constexpr int kPF = 2;             // LDS operand reads in flight (products ahead)
@@ -350,12 +355,23 @@ __global__ __launch_bounds__(64 * dq_waves<SPARSE>(), SPARSE ? 2 : 1) void fa_bw
 // Software pipeline over 32-query halves of the 64-query tiles, one wave per
 // SIMD: while the VALU turns S, dP of one half into Z and dS, the matrix cores
 // already compute S, dP of the next half; then dV, dK take the first half's
-// products.  Q/dO tiles are triple-buffered (t in use, t + 1 read by the
-// look-ahead products, t + 2 landing).
+// products.  Q/dO tiles are multi-buffered in LDS (kv_buffers: t in use,
+// t + 1 read by the look-ahead products, later tiles landing).
+//
+// Geometry per head size.  Up to 192 a workgroup accumulates every column of
+// dK and dV of its keys.  At 256 the accumulators (256 registers) and the K, V
+// fragments (128) do not fit one wave, so the columns are split over
+// kv_splits workgroups per key block: each recomputes S and dP over all of D
+// and accumulates D / kv_splits columns.  The LDS holds four Q/dO tile
+// buffers up to 128, three up to 192 (120-144 KB) and two at 256 (128 KB).
+template <int D> constexpr int kv_splits() { return D > 192 ? 2 : 1; }
+template <int D> constexpr int kv_cols() { return D / kv_splits<D>(); }
+template <int D> constexpr int kv_buffers() { return D <= 128 ? 4 : (D <= 192 ? 3 : 2); }
+
 template <int D, bool BF16>
 struct KVState {
-  u32x4 kf[D / 16], vf[D / 16];  // K, V fragments of this lane's key
-  f32x16 dv[D / 32], dk[D / 32];
+  u32x4 kf[D / 16], vf[D / 16];                // K, V fragments of this lane's key (all D)
+  f32x16 dv[kv_cols<D>() / 32], dk[kv_cols<D>() / 32];  // the accumulated columns
 };
 
 // Per-lane LDS read addresses of one tile: operand reads (chunk pairs s even
@@ -559,7 +575,7 @@ __device__ __forceinline__ f32x4 lds_f32x4(uint32_t addr) {
 // after look-ahead product i (the caller issues its tile loads there, so that
 // their issue overlaps the products).  On return sacc, pacc, zpk[0..3],
 // spk[0..3] describe the next half.
-template <int D, bool BF16, bool MASK, bool DROPOUT, typename Hook, typename Mid>
+template <int D, bool BF16, bool MASK, bool DROPOUT, bool PF_NEXT, typename Hook, typename Mid>
 __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st, f32x16& sacc, f32x16& pacc,
                                           uint32_t (&zpk)[8], uint32_t (&spk)[8], u32x4 (&pf)[4],
                                           const TileAddr& nop, const TileAddr& nnop, int nnqt, const TileAddr& tr,
@@ -567,16 +583,19 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
                                           Hook&& hook, Mid&& mid) {
   using T = MTile<D, kBR>;
   constexpr int kNP = D / 8;  // look-ahead products (S and dP, D/16 k-steps each)
-  constexpr int kPF = D >= 64 ? 4 : 2;  // LDS operand reads in flight (products ahead)
+  // LDS operand reads in flight (products ahead); two at 256, where the
+  // register file is full
+  constexpr int kPF = (D >= 64 && D <= 192) ? 4 : 2;
   static_assert(kNP >= 2 * kPF, "prefetch window exceeds a phase");
   auto opnd = [&](const TileAddr& t, int qt, int i) {
     const int s = i >> 1;
     const uint32_t base = (i & 1) ? ((s & 1) ? t.g1 : t.g0) : ((s & 1) ? t.q1 : t.q0);
     return lds_read16_at(base + T::opnd_off(qt, s));
   };
-  constexpr int kNA = 2 * 2 * (D / 32);  // dV, dK products
+  constexpr int kDT = kv_cols<D>() / 32;  // accumulated 32-column tiles (tr addresses start at the first)
+  constexpr int kNA = 2 * 2 * kDT;         // dV, dK products
   auto tr_pair = [&](int j) {
-    const int mm = j / (2 * (D / 32)), dt = (j >> 1) % (D / 32);
+    const int mm = j / (2 * kDT), dt = (j >> 1) % kDT;
     const uint32_t o = T::tr_off(2 * cur.qt + mm, dt);
     const uint32_t b0 = (j & 1) ? tr.q0 : tr.g0, b1 = (j & 1) ? tr.q1 : tr.g1;
     const u32x2 x0 = lds_read_tr_at(b0 + o), x1 = lds_read_tr_at(b1 + o);
@@ -647,7 +666,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kNA; ++j) {
-    const int mm = j / (2 * (D / 32)), dt = (j >> 1) % (D / 32);
+    const int mm = j / (2 * kDT), dt = (j >> 1) % kDT;
     if (j & 1)
       st.dk[dt] = mfma32<BF16>(sf[mm], tb[j], st.dk[dt]);
     else
@@ -655,7 +674,7 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
     if (j == 0) mfma_vgpr_wait();  // ns, np (read from j = kLag on) are complete
     if (j + kPF < kNA)
       tb[j + kPF] = tr_pair(j + kPF);
-    else
+    else if (PF_NEXT)  // (otherwise the caller reads them once they have landed)
       pf[j + kPF - kNA] = opnd(nnop, nnqt, j + kPF - kNA);
     if (j >= kLag) {
       constexpr int kSpan = kNA - kLag;
@@ -683,7 +702,9 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   using T = MTile<D, kBR>;
-  constexpr int kNB = 4;  // Q/dO/LSE/D tile buffers
+  constexpr int kNB = kv_buffers<D>();  // Q/dO/LSE/D tile buffers
+  constexpr int kAhead = kNB - 1;       // tiles loaded ahead of the one in use
+  constexpr int kDA = kv_cols<D>();     // dK, dV columns this workgroup accumulates
   __shared__ __attribute__((aligned(1024))) uint16_t qs[kNB][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t gs[kNB][T::kElems];
   __shared__ __attribute__((aligned(16))) float ls[kNB][kBR];
@@ -700,11 +721,13 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
 
-  // Workgroup -> (b, h, key block): heads fastest; causal: the first key
-  // blocks see the most queries and go first.
+  // Workgroup -> (b, h, key block, column split): heads fastest; causal: the
+  // first key blocks see the most queries and go first.
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
-  const int kb = blockIdx.x / BH;
+  const int kb = blockIdx.x / BH / kv_splits<D>();
+  const int split = blockIdx.x / BH % kv_splits<D>();
+  const int c0 = split * kDA;  // first accumulated column
   const int b = bh / a.H;
   const int h = bh % a.H;
   int start, L;
@@ -739,7 +762,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
       asm volatile("" : "+v"(st.vf[s]));
     }
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+    for (int dt = 0; dt < kDA / 32; ++dt) {
       st.dv[dt] = f32x16{};
       st.dk[dt] = f32x16{};
       // the accumulators live in AGPRs for the whole loop (only the matrix
@@ -781,7 +804,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   };
 
   const uint32_t ob0 = T::opnd_base(lane, 0), ob1 = T::opnd_base(lane, 1);
-  const uint32_t tb0 = T::tr_base(lane, 0), tb1 = T::tr_base(lane, 1);
+  // transpose reads (dV, dK products) start at the first accumulated column:
+  // 32 columns are 2 KB of a tile
+  const uint32_t tb0 = T::tr_base(lane, 0) + 64 * c0, tb1 = T::tr_base(lane, 1) + 64 * c0;
 
   // Visited query tiles: all tiles 0 .. ntiles-1 (from i_begin), or
   // (block-sparse) the listed ones.  Buffers follow the position k in that
@@ -838,11 +863,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
       T::load(x.qr, x.qdst, row_bytes, (k >> 1) * kWaves + w, lane);
   };
 
+  // prologue loads: tiles 0 and (with two or more tiles ahead) 1 landed,
+  // tiles 2 .. kAhead - 1 in flight
   if (n_list > 0) issue_tile(i_begin + t_first * kBR, 0);
-  if (n_list > 1) issue_tile(i_begin + tile_at(1) * kBR, 1);
+  if (kAhead >= 2 && n_list > 1) issue_tile(i_begin + tile_at(1) * kBR, 1);
   wait_vmem();
   __syncthreads();
-  {
+  if constexpr (kAhead >= 3) {
+    static_assert(kAhead == 3, "at most three tiles ahead");
     const TileLoads x = tile_loads(n_list > 2 ? tile_at(2) : -1, 2);
 #pragma unroll
     for (int k = 0; k <= 2 * kNU; ++k) tile_load_part(x, k);
@@ -882,23 +910,24 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // Iteration at position t of the visited tiles (tiles tk, tk1, tk3 at
-  // positions t, t+1, t+3; -1 past the end).
-  auto iteration = [&](int t, int tk, int tk1, int tk3, auto mask) {
+  // Iteration at position t of the visited tiles (tiles tk, tk1, tka at
+  // positions t, t+1, t+kAhead; -1 past the end).
+  auto iteration = [&](int t, int tk, int tk1, int tka, auto mask) {
     constexpr bool kMask = decltype(mask)::value;
     const int buf = t % kNB;
     const int nbuf = (t + 1) % kNB;
     const int i0 = i_begin + tk * kBR;
-    // tile t + 1 has landed (loads complete in order: only tile t + 2's may
-    // still be in flight); every wave is done with tile t - 1's buffers (the
-    // reads still in flight here touch tiles t and t + 1 only)
-    wait_vmem_n<kTileLoads>();
+    // With two or more tiles ahead, tile t + 1 has landed here (loads
+    // complete in order: only tiles t + 2 .. t + kAhead - 1 may still be in
+    // flight).  Every wave is done with tile t - 1's buffers (the reads still
+    // in flight here touch tiles t and t + 1 only).
+    if constexpr (kAhead >= 2) wait_vmem_n<(kAhead - 2) * kTileLoads>();
     barrier_keep_lds_reads();
 
-    // Loads of tile t + 3 into buffer (t + 3) % kNB (tile t - 1's), spread
-    // over the first half's look-ahead products: Q and dO blocks at even
-    // products, LSE or D at product 1.
-    const TileLoads x = tile_loads(tk3, (t + 3) % kNB);
+    // Loads of tile t + kAhead into buffer (t + kAhead) % kNB (tile t - 1's),
+    // spread over the first half's look-ahead products: Q and dO blocks at
+    // even products, LSE or D at product 1.
+    const TileLoads x = tile_loads(tka, (t + kAhead) % kNB);
     static_assert(4 * kNU - 2 < D / 8, "the look-ahead products must carry every tile load");
     // Dropout: the next tile's keep bits, hashed in 32 slices spread over
     // the look-ahead products of both halves (where the VALU has room next
@@ -937,16 +966,29 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     // discarded; doing it anyway keeps the tile one basic block.  Masked
     // tiles come first, so the look-ahead into the next tile may use this
     // tile's masking.
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj, h2,
-                                       load_hook, []() {});
+    dkdv_half<D, BF16, kMask, DROPOUT, (kAhead >= 2)>(a, st, sacc, pacc, zpk, spk, pf, op, nop, 0, tr, h0, h1, kj,
+                                                      h2, load_hook, []() {});
     if constexpr (DROPOUT) {
       // every slice ran in the first half and the second half's phase 1
       static_assert(2 * (D / 8) * ((32 + 2 * (D / 8) - 1) / (2 * (D / 8))) >= 32, "keep slices do not fit");
     }
-    dkdv_half<D, BF16, kMask, DROPOUT>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2,
-                                       second_hook, [&]() __attribute__((always_inline)) {
-                                         if constexpr (DROPOUT) n0.kb = kt.bits & 0xffffu;
-                                       });
+    if constexpr (kAhead == 1) {
+      // one tile ahead: tile t + 1 was issued at the start of this iteration;
+      // wait for every wave's share before reading the first operands of its
+      // look-ahead products (which the first half leaves to this point)
+      wait_vmem();
+      barrier_keep_lds_reads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = i >> 1;
+        const uint32_t base = (i & 1) ? ((s & 1) ? nop.g1 : nop.g0) : ((s & 1) ? nop.q1 : nop.q0);
+        pf[i] = lds_read16_at(base + T::opnd_off(0, s));
+      }
+    }
+    dkdv_half<D, BF16, kMask, DROPOUT, true>(a, st, sacc, pacc, zpk, spk, pf, nop, nop, 1, tr, h1, n0, kj, h2,
+                                             second_hook, [&]() __attribute__((always_inline)) {
+                                               if constexpr (DROPOUT) n0.kb = kt.bits & 0xffffu;
+                                             });
     if constexpr (DROPOUT) kb_cur = kt.bits;
   };
   // Causal: only the first two tiles (queries j0 .. j0+127) hold queries
@@ -954,25 +996,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   int t = 0;
   int tk = n_list > 0 ? t_first : -1;
   int tk1 = n_list > 1 ? tile_at(1) : -1;
-  int tk2 = n_list > 2 ? tile_at(2) : -1;
+  auto tile_or_none = [&](int k) __attribute__((always_inline)) { return k < n_list ? tile_at(k) : -1; };
   if (CAUSAL)
     for (; t < n_list && tk < 2; ++t) {
-      const int tk3 = t + 3 < n_list ? tile_at(t + 3) : -1;
-      iteration(t, tk, tk1, tk3, std::true_type{});
+      iteration(t, tk, tk1, tile_or_none(t + kAhead), std::true_type{});
       tk = tk1;
-      tk1 = tk2;
-      tk2 = tk3;
+      tk1 = tile_or_none(t + 2);
     }
   for (; t < n_list; ++t) {
-    const int tk3 = t + 3 < n_list ? tile_at(t + 3) : -1;
-    iteration(t, tk, tk1, tk3, std::false_type{});
+    iteration(t, tk, tk1, tile_or_none(t + kAhead), std::false_type{});
     tk = tk1;
-    tk1 = tk2;
-    tk2 = tk3;
+    tk1 = tile_or_none(t + 2);
   }
 
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
+  for (int dt = 0; dt < kDA / 32; ++dt) {
     asm volatile("" : "+a"(st.dv[dt]));
     asm volatile("" : "+a"(st.dk[dt]));
   }
@@ -983,12 +1021,12 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   // of the last iterations still write the tile buffers: wait for them.
   wait_vmem();
   __syncthreads();
-  constexpr int kRowE = D + 8;  // padded LDS row, 16-bit elements
+  constexpr int kRowE = kDA + 8;  // padded LDS row, 16-bit elements
   uint16_t* stage_k = qs[0];    // 128 rows x kRowE elements fit in each set of tile buffers
   uint16_t* stage_v = gs[0];
   static_assert(kBKV * kRowE <= kNB * T::kElems, "epilogue staging does not fit");
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < kDA / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * w + 8 * (r >> 2) + 4 * h2 + (r & 3);
@@ -997,7 +1035,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
       stage_v[row * kRowE + dt * 32 + l32] = (uint16_t)(pk >> 16);
     }
   __syncthreads();
-  constexpr int kCPR = D / 8;
+  constexpr int kCPR = kDA / 8;  // 16-byte chunks of the accumulated columns of a row
 #pragma unroll
   for (int u = 0; u < kBKV * kCPR / kThreads; ++u) {
     const int c = tid + kThreads * u;
@@ -1005,7 +1043,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const int col = (c % kCPR) * 8;
     const int j = j0 + row;
     if (j < L) {
-      const int64_t off = (int64_t)(start + j) * ld + (int64_t)h * D + col;
+      const int64_t off = (int64_t)(start + j) * ld + (int64_t)h * D + c0 + col;
       *reinterpret_cast<u32x4*>(a.dk + off) = *reinterpret_cast<const u32x4*>(&stage_k[row * kRowE + col]);
       *reinterpret_cast<u32x4*>(a.dv + off) = *reinterpret_cast<const u32x4*>(&stage_v[row * kRowE + col]);
     }
@@ -1013,15 +1051,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
-hipError_t launch_bwd_s(const AttnShape& s, const BwdArgs& args, int stages, hipStream_t stream) {
+hipError_t launch_bwd_s(const AttnShape& s, BwdArgs args, int stages, hipStream_t stream) {
+  args.nqb = (s.N + dq_rows<SPARSE, D>() - 1) / dq_rows<SPARSE, D>();
   if (stages & kBwdDq) {
     const int64_t nb = (int64_t)args.nqb * s.B * s.H;
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb),
-                       dim3(64 * dq_waves<SPARSE>()), 0, stream, args);
+                       dim3(64 * dq_waves<SPARSE, D>()), 0, stream, args);
   }
   if (stages & kBwdKV) {
-    const int64_t nb = (int64_t)args.nkb * s.B * s.H;
+    const int64_t nb = (int64_t)args.nkb * s.B * s.H * kv_splits<D>();
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb), dim3(kThreads),
                        0, stream, args);
@@ -1031,6 +1070,7 @@ hipError_t launch_bwd_s(const AttnShape& s, const BwdArgs& args, int stages, hip
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
 hipError_t launch_bwd_t(const AttnShape& s, const BwdArgs& args, int stages, hipStream_t stream) {
+  static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head sizes: multiples of 32 up to 256");
   return args.bmask ? launch_bwd_s<D, BF16, CAUSAL, DROPOUT, true>(s, args, stages, stream)
                     : launch_bwd_s<D, BF16, CAUSAL, DROPOUT, false>(s, args, stages, stream);
 }
@@ -1066,8 +1106,7 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
   a.B = s.B;
   a.H = s.H;
   a.N = s.N;
-  const int bq = s.bmask ? dq_rows<true>() : dq_rows<false>();
-  a.nqb = (s.N + bq - 1) / bq;
+  a.nqb = 0;  // set by the launcher from the workgroup size of the instance
   a.nkb = (s.N + kBKV - 1) / kBKV;
   a.scale = s.scale;
   a.scale_log2 = s.scale * kLog2e;
@@ -1081,8 +1120,14 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
     case 32: return s.bf16 ? launch_bwd_d<32, true>(s, a, stages, stream) : launch_bwd_d<32, false>(s, a, stages, stream);
     case 64: return s.bf16 ? launch_bwd_d<64, true>(s, a, stages, stream) : launch_bwd_d<64, false>(s, a, stages, stream);
     case 96: return s.bf16 ? launch_bwd_d<96, true>(s, a, stages, stream) : launch_bwd_d<96, false>(s, a, stages, stream);
-    default: return s.bf16 ? launch_bwd_d<128, true>(s, a, stages, stream)
-                           : launch_bwd_d<128, false>(s, a, stages, stream);
+    case 128: return s.bf16 ? launch_bwd_d<128, true>(s, a, stages, stream)
+                            : launch_bwd_d<128, false>(s, a, stages, stream);
+    case 160: return s.bf16 ? launch_bwd_d<160, true>(s, a, stages, stream)
+                            : launch_bwd_d<160, false>(s, a, stages, stream);
+    case 192: return s.bf16 ? launch_bwd_d<192, true>(s, a, stages, stream)
+                            : launch_bwd_d<192, false>(s, a, stages, stream);
+    default: return s.bf16 ? launch_bwd_d<256, true>(s, a, stages, stream)
+                           : launch_bwd_d<256, false>(s, a, stages, stream);
   }
 }
 

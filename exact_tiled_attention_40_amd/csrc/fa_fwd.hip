@@ -35,11 +35,15 @@
 namespace fa {
 namespace {
 
-// Dense: eight waves (two per SIMD, ping-pong), 256 queries share each K/V
-// tile.  Block-sparse: four waves (one 128-query mask row per workgroup, so
-// the tile list is exact), two workgroups per CU, no ping-pong.
-template <bool SPARSE> constexpr int waves() { return SPARSE ? 4 : 8; }
-template <bool SPARSE> constexpr int rows_per_wg() { return 32 * waves<SPARSE>(); }
+// Dense, heads up to 128: eight waves (two per SIMD, ping-pong), 256 queries
+// share each K/V tile.  Block-sparse: four waves (one 128-query mask row per
+// workgroup, so the tile list is exact), no ping-pong, two workgroups per CU
+// for heads up to 128.  Heads above 128: four waves, one per SIMD and one
+// workgroup per CU, so that each wave has the whole register file for its
+// larger output tile (and the K/V double buffers of up to 128 KB fit in LDS).
+template <bool SPARSE, int D> constexpr int waves() { return (SPARSE || D > 128) ? 4 : 8; }
+template <bool SPARSE, int D> constexpr int rows_per_wg() { return 32 * waves<SPARSE, D>(); }
+template <bool SPARSE, int D> constexpr int wgs_per_cu() { return (SPARSE && D <= 128) ? 2 : 1; }
 constexpr int kBC = 64;           // keys per tile
 // The partial output is rescaled only when a row max grows by more than this
 // many powers of two; otherwise the stale max stays the reference, so the
@@ -65,10 +69,10 @@ struct FwdArgs {
 };
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
-__global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>())) void fa_fwd_kernel(FwdArgs a) {
   using T = MTile<D, kBC>;
-  constexpr int kWaves = waves<SPARSE>();
-  constexpr int kBR = rows_per_wg<SPARSE>();
+  constexpr int kWaves = waves<SPARSE, D>();
+  constexpr int kBR = rows_per_wg<SPARSE, D>();
   constexpr int kNS = 2 * (D / 16);  // S^T products per tile (two 32-key tiles x D/16 k-steps)
   constexpr int kNO = 4 * (D / 32);  // O^T products per tile (four 16-key slices x D/32 tiles)
   constexpr int kPF = 3;             // LDS operand reads in flight (products ahead)
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_k
   // partial), and tile loads per wave per tile step
   constexpr int kPer = (T::kBlocks + kWaves - 1) / kWaves;
   constexpr int kLoads = 2 * kPer;
-  static_assert(SPARSE || kLoads == 2 || kLoads == 4, "softmax-phase load spreading assumes 2 or 4 loads");
+  static_assert(kWaves == 4 || kLoads == 2 || kLoads == 4, "softmax-phase load spreading assumes 2 or 4 loads");
   static_assert(kNS % kLoads == 0 && kNS / kLoads >= 2, "product-phase load spreading");
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
@@ -363,9 +367,9 @@ __global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_k
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(tlist[k]);
     else return k;
   };
-  // ping-pong group (dense); the block-sparse workgroup runs every wave as
-  // group 0 (no phase offset)
-  const int grp = SPARSE ? 0 : w / (kWaves / 2);
+  // ping-pong group (eight waves); the four-wave workgroups run every wave
+  // as group 0 (no phase offset)
+  const int grp = kWaves == 4 ? 0 : w / (kWaves / 2);
   auto skip_at = [&](int) __attribute__((always_inline)) -> bool { return false; };
 
   if (n_list > 0) {
@@ -468,21 +472,24 @@ __global__ __launch_bounds__(64 * waves<SPARSE>(), SPARSE ? 2 : 1) void fa_fwd_k
 }
 
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT>
-hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
+hipError_t launch_fwd_t(FwdArgs args, hipStream_t stream) {
   const bool sparse = args.bmask != nullptr;
+  const int br = sparse ? rows_per_wg<true, D>() : rows_per_wg<false, D>();
+  args.nqb = (args.N + br - 1) / br;
   const int64_t nblocks = (int64_t)args.nqb * args.B * args.H;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (sparse)
     hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, true>), dim3((unsigned)nblocks),
-                       dim3(64 * waves<true>()), 0, stream, args);
+                       dim3(64 * waves<true, D>()), 0, stream, args);
   else
     hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, false>), dim3((unsigned)nblocks),
-                       dim3(64 * waves<false>()), 0, stream, args);
+                       dim3(64 * waves<false, D>()), 0, stream, args);
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_fwd_d(const AttnShape& s, const FwdArgs& args, hipStream_t stream) {
+  static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head sizes: multiples of 32 up to 256");
   if (s.causal)
     return s.dropout ? launch_fwd_t<D, BF16, true, true>(args, stream)
                      : launch_fwd_t<D, BF16, true, false>(args, stream);
@@ -521,8 +528,7 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
   a.B = s.B;
   a.H = s.H;
   a.N = s.N;
-  const int br = s.bmask ? rows_per_wg<true>() : rows_per_wg<false>();
-  a.nqb = (s.N + br - 1) / br;
+  a.nqb = 0;  // set by the launcher from the workgroup size of the instance
   a.scale_log2 = s.scale * kLog2e;
   a.drop_thresh = s.drop_thresh;
   a.drop_rescale = s.drop_rescale;
@@ -537,8 +543,14 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
                            : launch_fwd_d<64, false>(s, a, stream);
     case 96: return s.bf16 ? launch_fwd_d<96, true>(s, a, stream)
                            : launch_fwd_d<96, false>(s, a, stream);
-    default: return s.bf16 ? launch_fwd_d<128, true>(s, a, stream)
-                           : launch_fwd_d<128, false>(s, a, stream);
+    case 128: return s.bf16 ? launch_fwd_d<128, true>(s, a, stream)
+                            : launch_fwd_d<128, false>(s, a, stream);
+    case 160: return s.bf16 ? launch_fwd_d<160, true>(s, a, stream)
+                            : launch_fwd_d<160, false>(s, a, stream);
+    case 192: return s.bf16 ? launch_fwd_d<192, true>(s, a, stream)
+                            : launch_fwd_d<192, false>(s, a, stream);
+    default: return s.bf16 ? launch_fwd_d<256, true>(s, a, stream)
+                           : launch_fwd_d<256, false>(s, a, stream);
   }
 }
 

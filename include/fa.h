@@ -55,10 +55,14 @@
  *     / 2^16 (within 2^-16 of dropout_p).  Forward and backward must get the
  *     same seed and dropout_p.  dropout_p == 0 runs the no-dropout kernels.
  *   - dtype is FA_DTYPE_F16 or FA_DTYPE_BF16 for every tensor except lse and
- *     the workspace (float32).  d must be 32, 64, 96 or 128: head sizes up to
- *     128 are the fused-kernel range in the tiemojia.cn article's list of
- *     when the fused kernel applies (its engineering-considerations part);
- *     the lab write-up, section 5.3, warns that kernels degrade past 192.
+ *     the workspace (float32).  d must be 32, 64, 96, 128, 160, 192 or 256.
+ *     Up to 128 is the fused-kernel range in the tiemojia.cn article's list
+ *     of when the fused kernel applies (its engineering-considerations
+ *     part); the larger heads run with one wave per SIMD (the output tile
+ *     needs the whole register file), and at 256 the key-side kernel
+ *     recomputes S and dP once per half of dK, dV's columns, so those
+ *     heads run at a lower rate -- the lab write-up, section 5.3, warns
+ *     that kernels degrade past 192.
  *   - Pointers must be 16-byte aligned and ld_qkv a multiple of 8; the
  *     token stride (ld_qkv, or H*d) may not exceed FA_MAX_TOKEN_STRIDE
  *     elements (FA_ERR_UNSUPPORTED otherwise: the kernels address a tile of
@@ -89,7 +93,7 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
     FA_ERR_BAD_SHAPE = 2,      /* B, H or N < 1, or a size overflows */
-    FA_ERR_UNSUPPORTED = 3,    /* d not in {32, 64, 96, 128}, unknown dtype,
+    FA_ERR_UNSUPPORTED = 3,    /* d not in {32, 64, 96, 128, 160, 192, 256}, unknown dtype,
                                   or a block-sparse N above FA_MASK_MAX_N */
     FA_ERR_BAD_ARGUMENT = 4,   /* scale not finite, dropout_p not in [0, 1) */
     FA_ERR_ALIGNMENT = 5,      /* pointer not 16-byte aligned or bad ld_qkv */

@@ -82,7 +82,7 @@ def fwd(lib, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), 1), (dict(lse=None), 1), (dict(o=None), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=70000, N=70000), 2),
-    (dict(d=16), 3), (dict(d=48), 3), (dict(d=160), 3), (dict(d=256), 3), (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(d=16), 3), (dict(d=48), 3), (dict(d=224), 3), (dict(d=288), 3), (dict(dtype=2), 3), (dict(dtype=-1), 3),
     (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=0.0), 4), (dict(scale=-1.0), 4),
     (dict(p=1.0), 4), (dict(p=-0.1), 4), (dict(p=float("nan")), 4),
     (dict(ld=100), 5), (dict(ld=127), 5), (dict(q=P + 8), 5), (dict(o=P + 2), 5), (dict(lse=P + 4), 5),
@@ -159,7 +159,7 @@ def test_block_sparse_forward_rejects_bad_arguments(lib):
     assert fwd_bs(lib, mask=None) == 1                    # no mask
     assert fwd_bs(lib, N=65537) == 3                      # longer than FA_MASK_MAX_N
     assert fwd_bs(lib, q=None) == 1                       # the dense checks still apply
-    assert fwd_bs(lib, d=256) == 3
+    assert fwd_bs(lib, d=224) == 3
     assert fwd_bs(lib, scale=float("nan")) == 4
     assert fwd_bs(lib, o=P + 2) == 5
 

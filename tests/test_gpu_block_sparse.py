@@ -83,6 +83,9 @@ CASES = [
     (2, 1, 1111, 128, "f16", False, 0.7),
     (1, 2, 600, 32, "bf16", True, 0.5),
     (1, 2, 500, 96, "f16", False, 0.4),
+    (1, 2, 640, 160, "bf16", True, 0.5),
+    (2, 1, 500, 192, "f16", False, 0.5),
+    (1, 2, 777, 256, "bf16", True, 0.4),
 ]
 
 

@@ -130,6 +130,9 @@ def check_probe(lengths, H, d, dtype, causal, p, seed, varlen, heads=None):
     ([5, 130, 77, 260], 2, 128, "bf16", True, 0.1, 99, True),
     ([70, 33], 1, 32, "f16", False, 0.25, 7, True),
     ([150, 90], 2, 96, "bf16", True, 0.2, 12345, True),
+    ([300, 77], 2, 160, "bf16", True, 0.1, 31, True),
+    ([200], 2, 192, "f16", False, 0.3, 32, False),
+    ([260, 130], 2, 256, "bf16", True, 0.2, 33, True),
 ])
 def test_keep_bits_through_fused_kernels(lengths, H, d, dtype, causal, p, seed, varlen):
     check_probe(lengths, H, d, dtype, causal, p, seed, varlen)

@@ -52,6 +52,17 @@ SMALL = [
     (1, 1, 1, 96, "f16", False),
     (2, 2, 300, 96, "bf16", True),
     (1, 2, 700, 96, "f16", False),
+    # heads above 128 (four waves, one per SIMD; 256: split dK/dV columns)
+    (1, 2, 1, 160, "bf16", True),
+    (2, 2, 200, 160, "f16", False),
+    (1, 3, 333, 160, "bf16", True),
+    (1, 1, 1, 192, "f16", False),
+    (2, 2, 257, 192, "bf16", True),
+    (1, 2, 600, 192, "f16", False),
+    (1, 1, 1, 256, "bf16", True),
+    (1, 2, 129, 256, "f16", False),
+    (2, 2, 300, 256, "bf16", True),
+    (1, 2, 777, 256, "bf16", False),
 ]
 
 
@@ -60,7 +71,7 @@ def test_forward_small(B, H, N, d, dtype, causal):
     check(workloads.custom(B, H, N, d, dtype, causal, seed=11 + N))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 192])
 def test_forward_packed_qkv(d):
     check(workloads.custom(2, 3, 150, d, "f16", False, packed=True, seed=5))
 
@@ -71,12 +82,18 @@ def test_forward_varlen_ragged(causal):
     check(x)
 
 
+@pytest.mark.parametrize("d,dtype", [(160, "f16"), (192, "bf16"), (256, "bf16")])
+def test_forward_varlen_ragged_large_heads(d, dtype):
+    check(workloads.custom(0, 2, 0, d, dtype, True, lengths=[1, 63, 64, 65, 200, 129, 7, 700], dropout_p=0.1,
+                           seed=d))
+
+
 def test_forward_varlen_dropout():
     x = workloads.custom(0, 2, 0, 128, "bf16", True, lengths=[5, 130, 77], dropout_p=0.3, seed=19)
     check(x)
 
 
-@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+@pytest.mark.parametrize("d,causal", [(64, False), (128, True), (160, True), (192, False), (256, True)])
 def test_forward_fixed_dropout(d, causal):
     check(workloads.custom(2, 2, 150, d, "f16", causal, dropout_p=0.2, seed=21))
 
