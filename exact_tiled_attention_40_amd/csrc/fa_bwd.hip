@@ -56,6 +56,7 @@ template <bool SPARSE, int D> constexpr int dq_wgs_per_cu() { return (SPARSE && 
 constexpr int kBC = 64;            // keys per tile of the dQ kernel
 constexpr int kBKV = 32 * kWaves;  // keys per dK/dV workgroup
 constexpr int kBR = 64;            // queries per tile of the dK/dV kernel
+constexpr int kKvHeadGroup = 2;    // dK/dV kernel: heads an XCD works on at a time
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100;
@@ -721,12 +722,29 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
 
-  // Workgroup -> (b, h, key block, column split): heads fastest; causal: the
-  // first key blocks see the most queries and go first.
+  // Workgroup -> (b, h, key block, column split).  Workgroups are dealt to
+  // the XCDs in turn (workgroup i to XCD i % 8).  When the head count allows,
+  // XCD x takes its heads (x, x + 8, ...) two at a time, key blocks first to
+  // last (causal: the first see the most queries) with the two heads
+  // alternating, so that the key blocks sharing an XCD's L2 stream the Q and
+  // dO tiles of two heads instead of all of its heads at once (measured at
+  // B 4, H 8, N 4096, d 128 causal: 151 MB fetched instead of about 470 MB,
+  // same time; one head at a time fetched 143 MB but ran 3% slower).  Other
+  // head counts: heads fastest.
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int kb = blockIdx.x / BH / kv_splits<D>();
-  const int split = blockIdx.x / BH % kv_splits<D>();
+  const int per_head = a.nkb * kv_splits<D>();
+  int bh, rest;
+  if (BH % (kXcds * kKvHeadGroup) == 0) {
+    const int m = blockIdx.x / kXcds;
+    const int g = m / (kKvHeadGroup * per_head), r = m % (kKvHeadGroup * per_head);
+    bh = blockIdx.x % kXcds + kXcds * (g * kKvHeadGroup + r % kKvHeadGroup);
+    rest = r / kKvHeadGroup;
+  } else {
+    bh = blockIdx.x % BH;
+    rest = blockIdx.x / BH;
+  }
+  const int kb = rest / kv_splits<D>();
+  const int split = rest % kv_splits<D>();
   const int c0 = split * kDA;  // first accumulated column
   const int b = bh / a.H;
   const int h = bh % a.H;

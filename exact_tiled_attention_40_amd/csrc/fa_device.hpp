@@ -178,6 +178,10 @@ __device__ __forceinline__ void buffer_load_lds4_addr(__amdgpu_buffer_rsrc_t r, 
       : "memory");
 }
 
+// MI355X: 8 XCDs, each with its own L2; the hardware deals a launch's
+// workgroups to them in turn.
+constexpr int kXcds = 8;
+
 // ------------------------------------------------------- block-sparse lists
 // Block masks have square blocks of kMaskBlock rows (queries) by kMaskBlock
 // columns (keys); the kernels' 64-row tiles are halves of mask blocks.

@@ -71,6 +71,11 @@ SMALL = [
     (1, 2, 129, 256, "f16", False),
     (2, 2, 300, 256, "bf16", True),
     (1, 2, 777, 256, "bf16", False),
+    # B * H a multiple of 16: the key-side kernel's workgroups run two heads
+    # at a time per XCD (with two column splits per key block at d = 256)
+    (2, 8, 300, 128, "bf16", True),
+    (1, 16, 129, 64, "f16", False),
+    (4, 8, 200, 256, "bf16", True),
 ]
 
 
