@@ -113,7 +113,9 @@ __global__ __launch_bounds__((64 * dq_waves<SPARSE, D>()), (dq_wgs_per_cu<SPARSE
   const int l32 = lane & 31;
 
   // Workgroup -> (b, h, query block): heads fastest (one head's blocks share
-  // an XCD when B*H is a multiple of 8); causal: longest blocks first.
+  // an XCD when B*H is a multiple of 8); causal: longest blocks first.  (Two
+  // heads at a time per XCD cut the fetched bytes at B 4, H 8, N 4096, d 128
+  // causal from 279 to 234 MB but ran 1.4% slower.)
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int rank = blockIdx.x / BH;
@@ -722,27 +724,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
 
-  // Workgroup -> (b, h, key block, column split).  Workgroups are dealt to
-  // the XCDs in turn (workgroup i to XCD i % 8).  When the head count allows,
-  // XCD x takes its heads (x, x + 8, ...) two at a time, key blocks first to
-  // last (causal: the first see the most queries) with the two heads
-  // alternating, so that the key blocks sharing an XCD's L2 stream the Q and
-  // dO tiles of two heads instead of all of its heads at once (measured at
-  // B 4, H 8, N 4096, d 128 causal: 151 MB fetched instead of about 470 MB,
-  // same time; one head at a time fetched 143 MB but ran 3% slower).  Other
-  // head counts: heads fastest.
+  // Workgroup -> (b, h, key block, column split): the key blocks of one
+  // head share an XCD, two heads at a time where B*H allows, key blocks first
+  // to last (causal: the first see the most queries).  The key blocks of a
+  // head start their causal query sweeps at different tiles, so with all of
+  // an XCD's heads at once its L2 could not hold their Q and dO tiles: at
+  // B 4, H 8, N 4096, d 128 causal this order fetches 151 MB instead of
+  // about 470 MB in the same time (one head at a time: 143 MB, 3% slower).
   const int BH = a.B * a.H;
-  const int per_head = a.nkb * kv_splits<D>();
   int bh, rest;
-  if (BH % (kXcds * kKvHeadGroup) == 0) {
-    const int m = blockIdx.x / kXcds;
-    const int g = m / (kKvHeadGroup * per_head), r = m % (kKvHeadGroup * per_head);
-    bh = blockIdx.x % kXcds + kXcds * (g * kKvHeadGroup + r % kKvHeadGroup);
-    rest = r / kKvHeadGroup;
-  } else {
-    bh = blockIdx.x % BH;
-    rest = blockIdx.x / BH;
-  }
+  xcd_head_order<kKvHeadGroup>(blockIdx.x, BH, a.nkb * kv_splits<D>(), bh, rest);
   const int kb = rest / kv_splits<D>();
   const int split = rest % kv_splits<D>();
   const int c0 = split * kDA;  // first accumulated column

@@ -182,6 +182,26 @@ __device__ __forceinline__ void buffer_load_lds4_addr(__amdgpu_buffer_rsrc_t r, 
 // workgroups to them in turn.
 constexpr int kXcds = 8;
 
+// Workgroup id -> (head bh = b*H + h, rank among the head's per_head
+// workgroups).  With heads fastest, workgroup i lands on XCD i % 8, so all
+// workgroups of one head share an XCD (and its L2) whenever B*H is a
+// multiple of 8.  When B*H is a multiple of 8*G, XCD x moreover takes its
+// heads (x, x + 8, ...) G at a time, ranks in order with the G heads
+// alternating, so that its L2 serves the tiles of G heads at a time instead
+// of all of its heads at once.
+template <int G>
+__device__ __forceinline__ void xcd_head_order(int id, int BH, int per_head, int& bh, int& rank) {
+  if (BH % (kXcds * G) == 0) {
+    const int m = id / kXcds;
+    const int g = m / (G * per_head), r = m % (G * per_head);
+    bh = id % kXcds + kXcds * (g * G + r % G);
+    rank = r / G;
+  } else {
+    bh = id % BH;
+    rank = id / BH;
+  }
+}
+
 // ------------------------------------------------------- block-sparse lists
 // Block masks have square blocks of kMaskBlock rows (queries) by kMaskBlock
 // columns (keys); the kernels' 64-row tiles are halves of mask blocks.

@@ -100,7 +100,10 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
   // Workgroup -> (b, h, query block).  Heads vary fastest so that, with the
   // round-robin dispatch over the 8 XCDs, every query block of one head lands
   // on the same XCD (K/V reuse in its L2) whenever B*H is a multiple of 8.
-  // Causal: the longest query blocks (last rows) are dispatched first.
+  // Causal: the longest query blocks (last rows) are dispatched first.  (Two
+  // heads at a time per XCD, as the key-side backward does, cut the fetched
+  // bytes at B 4, H 8, N 4096, d 128 causal from 197 to 145 MB but ran 2%
+  // slower: the longest-first order matters more here.)
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int rank = blockIdx.x / BH;
