@@ -2,7 +2,7 @@
 """Attention forward + backward throughput on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--block-density P] [--decode [--page-size P]]
+                    [--block-density P] [--keep-bits] [--decode [--page-size P]]
     python bench.py --compare-standard [--seqlens 512,1024,...] [--dropout P]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
@@ -515,6 +515,9 @@ def main() -> int:
     ap.add_argument("--page-size", type=int, default=0,
                     help="with --decode: time fa_decode_paged on the same caches split into pages of this many "
                          "tokens (a power of two) in shuffled order")
+    ap.add_argument("--keep-bits", action="store_true",
+                    help="dropout workloads: time fa_forward_keep / fa_backward_keep_stage (the forward stores "
+                         "its keep decisions, the backward reads them instead of hashing)")
     ap.add_argument("--head-dim", type=int, default=0,
                     help="run the chosen workload with this head size instead (32, 64, 96, 128, 160, 192 or 256)")
     ap.add_argument("--settle-s", type=float, default=1.5,
@@ -578,12 +581,27 @@ def main() -> int:
         bm = workloads.block_mask(wl.B, wl.H, wl.N, args.block_density, seed=wl.seed + 1000)
         kw["block_mask"] = bm.to(dev)
 
+    keep = None
+    if args.keep_bits:
+        if bm is not None or wl.dropout_p == 0:
+            print("--keep-bits times dense or varlen workloads with dropout", file=sys.stderr)
+            return 2
+        keep = torch.empty(fa.fa_dropout_bits_size(wl.B, wl.N, wl.H), dtype=torch.uint8, device=dev)
+
     def step(ev=None):
         if ev: ev[0].record(stream)
-        fa.fa_forward(q, k, v, out=o, lse=lse, stream=stream, **kw)
+        if keep is None:
+            fa.fa_forward(q, k, v, out=o, lse=lse, stream=stream, **kw)
+        else:
+            fa.fa_forward_keep(q, k, v, keep_bits=keep, out=o, lse=lse, stream=stream, **kw)
         if ev: ev[1].record(stream)
         for s in range(2):
-            fa.fa_backward_stage(s, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream, **kw)
+            if keep is None:
+                fa.fa_backward_stage(s, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream,
+                                     **kw)
+            else:
+                fa.fa_backward_keep_stage(s, q, k, v, o, lse, do, keep_bits=keep, dq=dq, dk=dk, dv=dv,
+                                          workspace=ws, stream=stream, **kw)
             if ev: ev[2 + s].record(stream)
 
     # W warm-up steps, repeated until at least --settle-s seconds have passed:
@@ -650,6 +668,7 @@ def main() -> int:
         "config": {"workload": wl.name + (f"_blocksparse{args.block_density:g}" if bm is not None else ""),
                    "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
                    "dropout_p": wl.dropout_p, "packed_qkv": wl.packed,
+                   **({"dropout_keep_bits": True} if keep is not None else {}),
                    **({"block_density": args.block_density, "mask_blocks_on": int(bm.sum()),
                        "mask_blocks": int(bm.numel()), "visible_pairs": pairs} if bm is not None else {}),
                    **({"varlen": True, "total_tokens": int(sum(x.lengths)), "visible_pairs": pairs}

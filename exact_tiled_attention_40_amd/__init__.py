@@ -15,19 +15,24 @@ from ._binding import (  # noqa: F401
     FA_MASK_MAX_N,
     FA_NOALLOC_MAX_ROWS,
     fa_backward,
+    fa_backward_keep,
+    fa_backward_keep_stage,
     fa_backward_noalloc,
     fa_backward_stage,
     fa_backward_workspace_size,
     fa_decode,
     fa_decode_paged,
     fa_decode_workspace_size,
+    fa_dropout_bits_size,
     fa_dropout_mask,
     fa_forward,
+    fa_forward_keep,
     fa_strerror,
     library_path,
 )
 
 __all__ = [
-    "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_DECODE_MAX_Q", "FA_MASK_BLOCK", "FA_MASK_MAX_N", "FA_NOALLOC_MAX_ROWS", "fa_backward", "fa_backward_noalloc",
-    "fa_backward_stage", "fa_backward_workspace_size", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size", "fa_dropout_mask", "fa_forward", "fa_strerror", "library_path",
+    "FAError", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_DECODE_MAX_Q", "FA_MASK_BLOCK", "FA_MASK_MAX_N", "FA_NOALLOC_MAX_ROWS", "fa_backward", "fa_backward_keep",
+    "fa_backward_keep_stage", "fa_backward_noalloc", "fa_backward_stage", "fa_backward_workspace_size", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size", "fa_dropout_bits_size", "fa_dropout_mask", "fa_forward", "fa_forward_keep",
+    "fa_strerror", "library_path",
 ]

@@ -58,6 +58,14 @@ def _load():
     lib.fa_backward_block_sparse.restype = i
     lib.fa_backward_block_sparse_stage.argtypes = [i] + lib.fa_backward_block_sparse.argtypes
     lib.fa_backward_block_sparse_stage.restype = i
+    lib.fa_dropout_bits_size.argtypes = [i, i, i]
+    lib.fa_dropout_bits_size.restype = ctypes.c_size_t
+    lib.fa_forward_keep.argtypes = lib.fa_forward.argtypes + [vp, ctypes.c_size_t]
+    lib.fa_forward_keep.restype = i
+    lib.fa_backward_keep.argtypes = lib.fa_backward.argtypes + [vp, ctypes.c_size_t]
+    lib.fa_backward_keep.restype = i
+    lib.fa_backward_keep_stage.argtypes = [i] + lib.fa_backward_keep.argtypes
+    lib.fa_backward_keep_stage.restype = i
     lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
@@ -170,6 +178,44 @@ def fa_forward(q, k, v, *, scale=None, causal=False, cu_seqlens=None, max_seqlen
     return out, lse
 
 
+def fa_dropout_bits_size(B: int, N: int, H: int) -> int:
+    """Bytes of the keep-bit buffer of fa_forward_keep / fa_backward_keep (0
+    when N exceeds FA_MASK_MAX_N)."""
+    return int(_lib.fa_dropout_bits_size(B, N, H))
+
+
+def _keep_bits(keep_bits, B, N, H, device):
+    if keep_bits is None:
+        return None, 0
+    if keep_bits.device != device or not keep_bits.is_contiguous():
+        raise ValueError("keep_bits must be a contiguous tensor on q's device")
+    return _ptr(keep_bits), keep_bits.numel() * keep_bits.element_size()
+
+
+def fa_forward_keep(q, k, v, *, keep_bits, scale=None, causal=False, cu_seqlens=None, max_seqlen=None,
+                    dropout_p=0.0, seed=0, out=None, lse=None, stream=None):
+    """fa_forward that also stores its dropout decisions into ``keep_bits``
+    (a device buffer of fa_dropout_bits_size(B, N, H) bytes, e.g. uint8 or
+    int32; unused, and may be None, when dropout_p == 0).  Returns (o, lse)."""
+    _same_geometry(q, k, v)
+    if q.dtype not in _DTYPES:
+        raise FAError(3, fa_strerror(3))
+    B, N, H, d, ld = _geometry(q, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    _check_like("lse", lse, q.shape[:-1], torch.float32, q.device)
+    kb, kb_bytes = _keep_bits(keep_bits, B, N, H, q.device)
+    _check(_lib.fa_forward_keep(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
+                                int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
+                                _stream(stream), _DTYPES[q.dtype], ld, kb, kb_bytes))
+    return out, lse
+
+
 def fa_backward_workspace_size(B: int, N: int, H: int, d: int) -> int:
     return int(_lib.fa_backward_workspace_size(B, N, H, d))
 
@@ -198,8 +244,28 @@ def fa_backward_stage(stage, q, k, v, o, lse, dout, *, scale=None, causal=False,
                      workspace=workspace, stream=stream, block_mask=block_mask)
 
 
+def fa_backward_keep(q, k, v, o, lse, dout, *, keep_bits, scale=None, causal=False, cu_seqlens=None,
+                     max_seqlen=None, dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """fa_backward reading the dropout decisions fa_forward_keep stored in
+    ``keep_bits`` (same shapes, lengths, dropout_p and seed)."""
+    return _backward(None, q, k, v, o, lse, dout, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
+                     max_seqlen=max_seqlen, dropout_p=dropout_p, seed=seed, dq=dq, dk=dk, dv=dv,
+                     workspace=workspace, stream=stream, keep_bits=keep_bits, keep=True)
+
+
+def fa_backward_keep_stage(stage, q, k, v, o, lse, dout, *, keep_bits, scale=None, causal=False, cu_seqlens=None,
+                           max_seqlen=None, dropout_p=0.0, seed=0, dq=None, dk=None, dv=None, workspace=None,
+                           stream=None):
+    """One stage of fa_backward_keep (0: D and dQ, 1: dK and dV)."""
+    if dq is None or dk is None or dv is None or workspace is None:
+        raise ValueError("fa_backward_keep_stage needs explicit dq, dk, dv and workspace")
+    return _backward(int(stage), q, k, v, o, lse, dout, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
+                     max_seqlen=max_seqlen, dropout_p=dropout_p, seed=seed, dq=dq, dk=dk, dv=dv,
+                     workspace=workspace, stream=stream, keep_bits=keep_bits, keep=True)
+
+
 def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_seqlen, dropout_p, seed, dq, dk,
-              dv, workspace, stream, block_mask=None):
+              dv, workspace, stream, block_mask=None, keep_bits=None, keep=False):
     _same_geometry(q, k, v)
     if q.dtype not in _DTYPES:
         raise FAError(3, fa_strerror(3))
@@ -222,7 +288,13 @@ def _backward(stage, q, k, v, o, lse, dout, *, scale, causal, cu_seqlens, max_se
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
             float(scale), int(bool(causal)), _ptr(cu_seqlens), float(dropout_p), int(seed) & (2**64 - 1),
             _stream(stream), _DTYPES[q.dtype], ld, _ptr(workspace), workspace.numel() * workspace.element_size())
-    if block_mask is not None:
+    if keep:
+        kb, kb_bytes = _keep_bits(keep_bits, B, N, H, q.device)
+        if stage is None:
+            _check(_lib.fa_backward_keep(*args, kb, kb_bytes))
+        else:
+            _check(_lib.fa_backward_keep_stage(stage, *args, kb, kb_bytes))
+    elif block_mask is not None:
         m = _block_mask(block_mask, B, H, N, q.device)
         if stage is None:
             _check(_lib.fa_backward_block_sparse(*args, m))

@@ -46,6 +46,7 @@ int check_common(int B, int H, int N, int d, float scale, float dropout_p, int d
   s->seed = seed;
   s->bmask = nullptr;
   s->nb = 0;
+  s->keep_bits = nullptr;
   return FA_OK;
 }
 
@@ -62,14 +63,29 @@ int check_block_mask(const uint8_t* block_mask, int N, fa::AttnShape* s) {
 
 extern "C" {
 
+// Keep-bit additions to a checked launch description (the bits matter only
+// with dropout).
+static int check_keep_bits(const void* bits, size_t bytes, fa::AttnShape* s) {
+  if (!s->dropout) return FA_OK;
+  if (!bits) return FA_ERR_NULL_POINTER;
+  if (s->N > FA_MASK_MAX_N) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_dropout_bits_size(s->B, s->N, s->H);
+  if (need == 0 || bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(bits)) return FA_ERR_ALIGNMENT;
+  s->keep_bits = const_cast<uint32_t*>(static_cast<const uint32_t*>(bits));
+  return FA_OK;
+}
+
 static int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
                         int d, float scale, int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
-                        void* stream, int dtype, int64_t ld_qkv, const uint8_t* block_mask, bool sparse) {
+                        void* stream, int dtype, int64_t ld_qkv, const uint8_t* block_mask, bool sparse,
+                        uint32_t* keep_bits = nullptr, size_t keep_bits_bytes = 0, bool keep = false) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
   fa::AttnShape s;
   int rc = check_common(B, H, N, d, scale, dropout_p, dtype, ld_qkv, cu_seqlens, causal, seed, &s);
   if (rc != FA_OK) return rc;
   if (sparse && (rc = check_block_mask(block_mask, N, &s)) != FA_OK) return rc;
+  if (keep && (rc = check_keep_bits(keep_bits, keep_bits_bytes, &s)) != FA_OK) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGNMENT;
   const hipError_t e = fa::launch_forward(s, q, k, v, o, lse, static_cast<hipStream_t>(stream));
@@ -88,6 +104,20 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
                             uint64_t seed, void* stream, int dtype, int64_t ld_qkv, const uint8_t* block_mask) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, dropout_p, seed, stream, dtype,
                       ld_qkv, block_mask, true);
+}
+
+int fa_forward_keep(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                    float scale, int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                    void* stream, int dtype, int64_t ld_qkv, uint32_t* keep_bits, size_t keep_bits_bytes) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, dropout_p, seed, stream, dtype,
+                      ld_qkv, nullptr, false, keep_bits, keep_bits_bytes, true);
+}
+
+size_t fa_dropout_bits_size(int B, int N, int H) {
+  if (B < 1 || N < 1 || H < 1 || N > FA_MASK_MAX_N) return 0;
+  const uint64_t words = fa::keep_bits_words(B, N, H);
+  if (words == 0 || words > SIZE_MAX / 4) return 0;
+  return (size_t)(words * 4);
 }
 
 size_t fa_backward_workspace_size(int B, int N, int H, int d) {
@@ -131,11 +161,13 @@ static int backward_impl(int stages, const void* q, const void* k, const void* v
                          const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                          int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
                          int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes,
-                         const uint8_t* block_mask, bool sparse) {
+                         const uint8_t* block_mask, bool sparse, const uint32_t* keep_bits = nullptr,
+                         size_t keep_bits_bytes = 0, bool keep = false) {
   fa::AttnShape s;
-  const int rc = check_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens, dropout_p,
-                                seed, dtype, ld_qkv, block_mask, sparse, &s);
+  int rc = check_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens, dropout_p,
+                          seed, dtype, ld_qkv, block_mask, sparse, &s);
   if (rc != FA_OK) return rc;
+  if (keep && (rc = check_keep_bits(keep_bits, keep_bits_bytes, &s)) != FA_OK) return rc;
   const size_t need = fa_backward_workspace_size(B, N, H, d);
   if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGNMENT;
@@ -148,6 +180,27 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes) {
   return backward_impl(fa::kBwdAll, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
                        dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, nullptr, false);
+}
+
+int fa_backward_keep(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                     int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream, int dtype,
+                     int64_t ld_qkv, void* workspace, size_t workspace_bytes, const uint32_t* keep_bits,
+                     size_t keep_bits_bytes) {
+  return backward_impl(fa::kBwdAll, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, nullptr, false, keep_bits,
+                       keep_bits_bytes, true);
+}
+
+int fa_backward_keep_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                           int causal, const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                           int dtype, int64_t ld_qkv, void* workspace, size_t workspace_bytes,
+                           const uint32_t* keep_bits, size_t keep_bits_bytes) {
+  if (stage < 0 || stage > 1) return FA_ERR_BAD_ARGUMENT;
+  return backward_impl(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, cu_seqlens,
+                       dropout_p, seed, stream, dtype, ld_qkv, workspace, workspace_bytes, nullptr, false, keep_bits,
+                       keep_bits_bytes, true);
 }
 
 int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,

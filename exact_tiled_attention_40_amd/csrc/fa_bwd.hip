@@ -74,6 +74,9 @@ struct BwdArgs {
   float* delta;   // D = rowsum(dO * O), [tokens, H]
   float* lse2;    // LSE * log2(e), [tokens, H]
   const int32_t* cu;
+  const uint32_t* kbits;  // keep-bit instantiations only: the forward's decisions (layout: fa_internal.h)
+  int nkt;                // ceil(N / 64)
+  int kbn;                // row stride of the keep-bit planes (N rounded up to 4)
   int64_t ld;
   int B, H, N, nqb, nkb;
   float scale;
@@ -90,9 +93,11 @@ __device__ __forceinline__ void seq_range(const BwdArgs& a, int b, int& start, i
 }
 
 // ---------------------------------------------------------------- dQ (+ D)
-template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE, bool KB = false>
 __global__ __launch_bounds__((64 * dq_waves<SPARSE, D>()), (dq_wgs_per_cu<SPARSE, D>())) void fa_bwd_dq_kernel(
     BwdArgs a) {
+  static_assert(!KB || (DROPOUT && !SPARSE), "keep bits: dense dropout instantiations only");
+  static_assert(!KB || kBC == 64, "keep-bit words cover 64-key tiles");
   using T = MTile<D, kBC>;
   constexpr int kWavesQ = dq_waves<SPARSE, D>();
   constexpr int kBQ = dq_rows<SPARSE, D>();
@@ -101,6 +106,9 @@ __global__ __launch_bounds__((64 * dq_waves<SPARSE, D>()), (dq_wgs_per_cu<SPARSE
   constexpr int kPF = 2;             // LDS operand reads in flight (products ahead)
   __shared__ __attribute__((aligned(1024))) uint16_t ks[2][T::kElems];
   __shared__ __attribute__((aligned(1024))) uint16_t vs[2][T::kElems];
+  // keep bits: the stored words of the workgroup's queries against the key
+  // tile of the buffer, two planes (keys 0-31, 32-63 of the tile) of kBQ rows
+  __shared__ __attribute__((aligned(1024))) uint32_t kbs[KB ? 2 : 1][KB ? 2 * kBQ : 4];
   // block-sparse: the key tiles the workgroup visits, in order
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];
   __shared__ uint8_t tflag[SPARSE ? kMaxSparseTiles : 1];
@@ -185,11 +193,28 @@ __global__ __launch_bounds__((64 * dq_waves<SPARSE, D>()), (dq_wgs_per_cu<SPARSE
   }
 
   const uint32_t ks0 = lds_addr(ks), vs0 = lds_addr(vs);
+  // the stored keep words of this head (at most 512 MB: N <= 65536)
+  const __amdgpu_buffer_rsrc_t kbr =
+      KB ? make_rsrc(a.kbits + (int64_t)bh * a.nkt * 2 * a.kbn, (uint32_t)((uint64_t)a.nkt * 2 * a.kbn * 4))
+         : make_rsrc(nullptr, 0u);
   auto issue_tile = [&](int j0, int buf) {
     const int rows = min(kBC, L - j0);
     const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)j0 * ld, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)j0 * ld, bytes);
+    if constexpr (KB) {
+      // 8 * kBQ bytes of stored words: 1 KB loads by the first kBQ / 128
+      // waves; lane l of load m takes the 16 bytes at m * 1024 + 16 l of the
+      // two planes laid end to end (rows past the head's buffer read as 0)
+      static_assert(kBQ % 128 == 0 && kBQ / 128 <= kWavesQ, "keep-bit loads");
+      if (w < kBQ / 128) {
+        const uint32_t f = (uint32_t)w * 1024 + 16 * lane;
+        const uint32_t plane = f / (4 * kBQ), r = (f % (4 * kBQ)) / 4;
+        const int t = j0 / kBC;
+        const uint32_t word = ((uint32_t)t * 2 + plane) * (uint32_t)a.kbn + (uint32_t)q0 + r;
+        buffer_load_lds16_addr(kbr, lds_addr(kbs[buf]) + (uint32_t)w * 1024, word * 4);
+      }
+    }
     // wave w loads blocks w, w + kWavesQ, ... (a partial last round when
     // the tile has fewer blocks than a multiple of the waves)
 #pragma unroll
@@ -280,10 +305,12 @@ __global__ __launch_bounds__((64 * dq_waves<SPARSE, D>()), (dq_wgs_per_cu<SPARSE
       uint32_t spk[8];
       // dropout: this lane's keep words of the four 8-key groups of the half
       uint32_t kw[2][2][2];  // [group pair][group of the pair][word]
-      if constexpr (DROPOUT) {
+      uint32_t kbw = 0;      // keep bits: key 8g + e of the lane's half at bit 8g + e
+      if constexpr (DROPOUT && !KB) {
         keep_words_pair(qi, j0 + kt * 32, h2, h, b, a.seed_lo, a.seed_hi, kw[0]);
         keep_words_pair(qi, j0 + kt * 32 + 16, h2, h, b, a.seed_lo, a.seed_hi, kw[1]);
       }
+      if constexpr (KB) kbw = kbs[cur][kt * kBQ + (qi - q0)] >> (4 * h2);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int kj4 = j0 + kt * 32 + 8 * g + 4 * h2;
@@ -294,7 +321,10 @@ __global__ __launch_bounds__((64 * dq_waves<SPARSE, D>()), (dq_wgs_per_cu<SPARSE
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, -lse2));
           if (kMask && ((CAUSAL && kj4 + e > qi) || kj4 + e >= L)) p = 0.f;
           float dp = pacc[r];
-          if constexpr (DROPOUT) dp *= keep16(kw[g >> 1][g & 1][e >> 1], e & 1, a.drop_thresh) ? a.drop_rescale : 0.f;
+          if constexpr (KB)
+            dp *= (kbw >> (8 * g + e)) & 1u ? a.drop_rescale : 0.f;
+          else if constexpr (DROPOUT)
+            dp *= keep16(kw[g >> 1][g & 1][e >> 1], e & 1, a.drop_thresh) ? a.drop_rescale : 0.f;
           ds[e] = p * (dp - delta);
         }
         spk[2 * g] = pack2<BF16>(ds[0], ds[1]);
@@ -702,8 +732,10 @@ __device__ __forceinline__ void dkdv_half(const BwdArgs& a, KVState<D, BF16>& st
   pacc = np;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE, bool KB = false>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  static_assert(!KB || (DROPOUT && !SPARSE), "keep bits: dense dropout instantiations only");
+  static_assert(!KB || (kBR == 64 && kBKV == 128), "keep-bit tiles: 64 queries by two 64-key words pairs");
   using T = MTile<D, kBR>;
   constexpr int kNB = kv_buffers<D>();  // Q/dO/LSE/D tile buffers
   constexpr int kAhead = kNB - 1;       // tiles loaded ahead of the one in use
@@ -713,6 +745,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float ls[kNB][kBR];
   __shared__ __attribute__((aligned(16))) float dls[kNB][kBR];
   __shared__ __attribute__((aligned(16))) float spare[64];
+  // keep bits: the stored words of a tile's 64 queries against the block's
+  // 128 keys, four planes of 64 rows (plane p: key tile 2*kb + p/2, key
+  // half p%2 -- the 32 keys of wave p)
+  __shared__ __attribute__((aligned(1024))) uint32_t kbs[KB ? kNB : 1][KB ? 256 : 4];
   // block-sparse: the query tiles the workgroup visits, in order
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];
   __shared__ uint8_t tflag[SPARSE ? kMaxSparseTiles : 1];
@@ -793,8 +829,22 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t qs0 = lds_addr(qs), gs0 = lds_addr(gs), ls0 = lds_addr(ls), dls0 = lds_addr(dls);
   const uint32_t hstride4 = (uint32_t)a.H * 4;  // bytes between consecutive tokens of LSE and D
 
+  // the stored keep words of this head (at most 512 MB: N <= 65536); lane l
+  // of the tile's 1 KB load takes rows 4*(l%16) .. +3 of plane l/16
+  const __amdgpu_buffer_rsrc_t kbr =
+      KB ? make_rsrc(a.kbits + (int64_t)bh * a.nkt * 2 * a.kbn, (uint32_t)((uint64_t)a.nkt * 2 * a.kbn * 4))
+         : make_rsrc(nullptr, 0u);
+  auto kbits_off = [&](int il) __attribute__((always_inline)) -> uint32_t {
+    if (il < 0) return 0xFFFFFFF0u;  // absent tile: out of range, the load fills zeros
+    const uint32_t p = (uint32_t)lane >> 4;
+    const uint32_t word = ((uint32_t)(j0 / 64 + (int)(p >> 1)) * 2 + (p & 1)) * (uint32_t)a.kbn + (uint32_t)il +
+                          4 * ((uint32_t)lane & 15);
+    return word * 4;
+  };
   auto issue_tile = [&](int i0, int buf) {
     const int rows = min(kBR, L - i0);
+    if constexpr (KB)
+      if (w == 2) buffer_load_lds16_addr(kbr, lds_addr(kbs[buf]), kbits_off(i0));
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qbase + (int64_t)i0 * ld, (uint32_t)(rows - 1) * row_bytes + D * 2);
     const __amdgpu_buffer_rsrc_t gr = make_rsrc(gbase + (int64_t)i0 * hd, (uint32_t)(rows - 1) * grow_bytes + D * 2);
     static_assert(T::kBlocks % kWaves == 0, "tile blocks must split evenly over the waves");
@@ -847,6 +897,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   struct TileLoads {
     __amdgpu_buffer_rsrc_t qr, gr, xr;
     uint32_t qdst, gdst, xdst;
+    uint32_t bdst, boff;  // keep bits (wave 2 loads them instead of its empty load)
   };
   const uint32_t xoff = (uint32_t)lane * hstride4;
   auto tile_loads = [&](int tkl, int lbuf) __attribute__((always_inline)) {
@@ -861,10 +912,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     x.qdst = qs0 + lbuf * T::kBytes;
     x.gdst = gs0 + lbuf * T::kBytes;
     x.xdst = w == 0 ? ls0 + lbuf * kBR * 4 : w == 1 ? dls0 + lbuf * kBR * 4 : lds_addr(spare);
+    if constexpr (KB) {
+      x.bdst = lds_addr(kbs[lbuf]);
+      x.boff = kbits_off(tkl >= 0 ? il : -1);
+    }
     return x;
   };
   auto tile_load_part = [&](const TileLoads& x, int k) __attribute__((always_inline)) {
-    if (k == 2 * kNU)
+    if (KB && k == 2 * kNU && w == 2)
+      buffer_load_lds16_addr(kbr, x.bdst, x.boff);
+    else if (k == 2 * kNU)
       buffer_load_lds4_addr(x.xr, x.xdst, xoff);
     else if (k & 1)
       T::load(x.gr, x.gdst, grow_bytes, (k >> 1) * kWaves + w, lane);
@@ -888,8 +945,22 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
   // pipeline prologue: S, dP and elements 0..7 of the first half, and the
   // first operands of its look-ahead products (half 1 of tile 0)
   // dropout keep bits of the tile in use (bit 16*half + element)
+  // keep bits: runs of four queries 8*run + 4*h2 + e of the tile in buffer
+  // buf against this lane's key (bit l32 of the row words of plane w), at
+  // bits e of the result
+  auto kb_run = [&](int buf, int run) __attribute__((always_inline)) -> uint32_t {
+    const u32x4 wd = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(
+        lds_addr(kbs[buf]) + 4 * (64 * w + 8 * run + 4 * h2));
+    return ((wd[0] >> l32) & 1u) | (((wd[1] >> l32) & 1u) << 1) | (((wd[2] >> l32) & 1u) << 2) |
+           (((wd[3] >> l32) & 1u) << 3);
+  };
   uint32_t kb_cur = 0;
-  if constexpr (DROPOUT) kb_cur = dkdv_tile_keep(a, b, h, i_begin + t_first * kBR, h2, kj);
+  if constexpr (KB) {
+#pragma unroll
+    for (int run = 0; run < 8; ++run) kb_cur |= kb_run(0, run) << (4 * run);
+  } else if constexpr (DROPOUT) {
+    kb_cur = dkdv_tile_keep(a, b, h, i_begin + t_first * kBR, h2, kj);
+  }
   f32x16 sacc, pacc;
   uint32_t zpk[8], spk[8];
   u32x4 pf[4];
@@ -942,9 +1013,18 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     // the look-ahead products of both halves (where the VALU has room next
     // to the matrix cores); the second half's phase 2 reads them through n0.
     KeepTask kt;
+    if constexpr (KB) kt.bits = 0;
     const int next_i0 = i_begin + max(tk1, 0) * kBR;
     auto keep_hook = [&](int half, int i) __attribute__((always_inline)) {
-      if constexpr (DROPOUT) {
+      if constexpr (KB) {
+        // the next tile's stored bits (landed: loaded kAhead tiles ahead, or,
+        // one ahead, waited for between the halves), read in the second half
+        constexpr int kRuns = (8 + D / 8 - 1) / (D / 8);  // runs per look-ahead product
+        if (half == 1)
+#pragma unroll
+          for (int run = i * kRuns; run < (i + 1) * kRuns && run < 8; ++run)
+            kt.bits |= kb_run(nbuf, run) << (4 * run);
+      } else if constexpr (DROPOUT) {
         constexpr int kPer = (32 + 2 * (D / 8) - 1) / (2 * (D / 8));  // slices per look-ahead product
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -1062,17 +1142,28 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
 hipError_t launch_bwd_s(const AttnShape& s, BwdArgs args, int stages, hipStream_t stream) {
   args.nqb = (s.N + dq_rows<SPARSE, D>() - 1) / dq_rows<SPARSE, D>();
+  // keep-bit instances: dense dropout with stored decisions
+  constexpr bool kKB = DROPOUT && !SPARSE;
+  const bool kb = kKB && args.kbits != nullptr;
   if (stages & kBwdDq) {
     const int64_t nb = (int64_t)args.nqb * s.B * s.H;
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb),
-                       dim3(64 * dq_waves<SPARSE, D>()), 0, stream, args);
+    if (kb)
+      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE, kKB>), dim3((unsigned)nb),
+                         dim3(64 * dq_waves<SPARSE, D>()), 0, stream, args);
+    else
+      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb),
+                         dim3(64 * dq_waves<SPARSE, D>()), 0, stream, args);
   }
   if (stages & kBwdKV) {
     const int64_t nb = (int64_t)args.nkb * s.B * s.H * kv_splits<D>();
     if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb), dim3(kThreads),
-                       0, stream, args);
+    if (kb)
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE, kKB>), dim3((unsigned)nb),
+                         dim3(kThreads), 0, stream, args);
+    else
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, DROPOUT, SPARSE>), dim3((unsigned)nb),
+                         dim3(kThreads), 0, stream, args);
   }
   return hipGetLastError();
 }
@@ -1117,6 +1208,9 @@ hipError_t launch_backward(const AttnShape& s, const void* q, const void* k, con
   a.N = s.N;
   a.nqb = 0;  // set by the launcher from the workgroup size of the instance
   a.nkb = (s.N + kBKV - 1) / kBKV;
+  a.kbits = s.dropout && !s.bmask ? s.keep_bits : nullptr;
+  a.nkt = (s.N + 63) / 64;
+  a.kbn = keep_bits_rows(s.N);
   a.scale = s.scale;
   a.scale_log2 = s.scale * kLog2e;
   a.drop_thresh = s.drop_thresh;

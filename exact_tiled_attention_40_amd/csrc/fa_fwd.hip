@@ -66,10 +66,15 @@ struct FwdArgs {
   uint32_t seed_lo, seed_hi;
   const uint8_t* bmask;  // block-sparse instantiations only: [B, H, nb, nb]
   int nb;
+  uint32_t* kbits;  // keep-bit instantiations only: the decisions drawn (layout: fa_internal.h)
+  int nkt;          // ceil(N / 64)
+  int kbn;          // row stride of the keep-bit planes (N rounded up to 4)
 };
 
-template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE>
+template <int D, bool BF16, bool CAUSAL, bool DROPOUT, bool SPARSE, bool KB = false>
 __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>())) void fa_fwd_kernel(FwdArgs a) {
+  static_assert(!KB || (DROPOUT && !SPARSE), "keep bits: dense dropout instantiations only");
+  static_assert(!KB || kBC == 64, "keep-bit words cover 64-key tiles");
   using T = MTile<D, kBC>;
   constexpr int kWaves = waves<SPARSE, D>();
   constexpr int kBR = rows_per_wg<SPARSE, D>();
@@ -124,6 +129,14 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
 
   const int qw = q0 + 32 * w;  // first query of this wave
   const int qi = qw + l32;     // query owned by this lane
+
+  // keep-bit store: this head's words through a buffer descriptor; lane half
+  // h2 writes word h2 of its query (rows past the end get an offset outside
+  // the buffer, so their stores are dropped)
+  const __amdgpu_buffer_rsrc_t kbr =
+      KB ? make_rsrc(a.kbits + (int64_t)bh * a.nkt * 2 * a.kbn, (uint32_t)((uint64_t)a.nkt * 2 * a.kbn * 4))
+         : make_rsrc(nullptr, 0u);
+  const uint32_t kb_off = KB && qi < L ? (uint32_t)(h2 * a.kbn + qi) * 4u : 0x80000000u;
 
   // Q fragment: B operand of S^T = K Q^T (column = query, K slice = head dim);
   // rows past the end read as zeros.
@@ -261,6 +274,16 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // keep bits of the last vector phase, stored by kb_flush after the slot's
+  // barrier: a store issued just before a full vmcnt wait would stall on its
+  // write acknowledgement
+  uint32_t kb_word = 0;
+  int kb_tile = 0;
+  auto kb_flush = [&]() __attribute__((always_inline)) {
+    if constexpr (KB)
+      __builtin_amdgcn_raw_buffer_store_b32(kb_word, kbr, kb_off, (uint32_t)kb_tile * 8u * (uint32_t)a.kbn, 0);
+  };
+
   // Vector phase of tile t: mask, online softmax of sacc (register r of key
   // half kt holds key t*kBC + kt*32 + 8*(r/4) + 4*h2 + r%4), dropout, and the
   // P^T operands of the next matrix phase.
@@ -317,6 +340,7 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
     }
     l_run += rs;
     if constexpr (DROPOUT) {
+      uint32_t kbw[2] = {0u, 0u};  // keep bits of this lane's keys of key half kt (bit 16gp + 8u + e)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -327,9 +351,21 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
 #pragma unroll
           for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (!keep16(kw[u][e >> 1], e & 1, a.drop_thresh)) sacc[kt][4 * (2 * gp + u) + e] = 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const bool keep = keep16(kw[u][e >> 1], e & 1, a.drop_thresh);
+              if (!keep) sacc[kt][4 * (2 * gp + u) + e] = 0.f;
+              if constexpr (KB) kbw[kt] |= keep ? 1u << (16 * gp + 8 * u + e) : 0u;
+            }
         }
+      if constexpr (KB) {
+        // the two lanes of a query hold alternate nibbles of each word (lane
+        // half 1 the high ones): after the swap lane half h2 holds its
+        // word h2 (keys 32*h2 .. 32*h2+31) as low nibbles in x, high in y
+        uint32_t x = kbw[0], y = kbw[1];
+        permlane32_swap(x, y);
+        kb_word = x | (y << 4);
+        kb_tile = t;
+      }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -424,6 +460,7 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
       else v_phase(tk, false, skip, no_hook);
       if (g == 0 && k > 0) wait_vmem();
       __syncthreads();
+      kb_flush();
       if constexpr (g == 0) m_phase(k, true, loads);
       else m_phase(k, true, no_hook);
       if (g == 1) wait_vmem();
@@ -441,6 +478,7 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
       if (mine) v_phase(tk, true, skip_at(k), no_hook);
       if (g == 0 && k > 0) wait_vmem();
       __syncthreads();
+      if (mine) kb_flush();
       if (g == 0)
         for (int u = 0; u < kLoads; ++u) load_part(k, tk1, tk2, u);
       if (mine) m_phase(k, false, no_hook);
@@ -484,6 +522,9 @@ hipError_t launch_fwd_t(FwdArgs args, hipStream_t stream) {
   if (sparse)
     hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, true>), dim3((unsigned)nblocks),
                        dim3(64 * waves<true, D>()), 0, stream, args);
+  else if (DROPOUT && args.kbits)
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, false, DROPOUT>), dim3((unsigned)nblocks),
+                       dim3(64 * waves<false, D>()), 0, stream, args);
   else
     hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, DROPOUT, false>), dim3((unsigned)nblocks),
                        dim3(64 * waves<false, D>()), 0, stream, args);
@@ -539,6 +580,9 @@ hipError_t launch_forward(const AttnShape& s, const void* q, const void* k, cons
   a.seed_hi = (uint32_t)(s.seed >> 32);
   a.bmask = s.bmask;
   a.nb = s.nb;
+  a.kbits = s.dropout ? s.keep_bits : nullptr;
+  a.nkt = (s.N + 63) / 64;
+  a.kbn = keep_bits_rows(s.N);
   switch (s.d) {
     case 32: return s.bf16 ? launch_fwd_d<32, true>(s, a, stream)
                            : launch_fwd_d<32, false>(s, a, stream);

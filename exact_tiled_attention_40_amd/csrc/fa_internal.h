@@ -20,7 +20,28 @@ struct AttnShape {
   uint64_t seed;
   const uint8_t* bmask;    // block mask [B, H, nb, nb] (device) or nullptr: dense
   int nb;                  // mask blocks per side, ceil(N / 128)
+  // Dropout keep bits (device; dense and varlen only) or nullptr: the
+  // forward stores the decisions it draws, the backward reads them instead
+  // of hashing.  Word (((b*H + h) * nkt + t) * 2 + w) * Np + i holds, in bit
+  // k, the decision of query i against key 64t + 32w + k (local indices,
+  // nkt = ceil(N / 64), Np = N rounded up to a multiple of 4, so that every
+  // run of four rows the kernels move is 16-byte aligned).
+  uint32_t* keep_bits;
 };
+
+// Row stride (words) of the keep-bit planes of sequences of at most N tokens.
+inline int keep_bits_rows(int N) { return (N + 3) & ~3; }
+
+// Number of 32-bit words of the keep-bit buffer of B sequences of at most N
+// tokens with H heads (0 if it overflows 64 bits).
+inline uint64_t keep_bits_words(int B, int N, int H) {
+  const uint64_t nkt = ((uint64_t)N + 63) / 64;
+  const uint64_t heads = (uint64_t)B * (uint64_t)H;
+  if (heads == 0 || nkt == 0 || N < 1) return 0;
+  const uint64_t per_head = nkt * 2 * (uint64_t)keep_bits_rows(N);
+  if (per_head > UINT64_MAX / 8 / heads) return 0;
+  return per_head * heads;
+}
 
 // First token and length of sequence b of a batch of B sequences whose
 // longest is N.  Fixed length: b*N and N.  Varlen: from the prefix sums cu

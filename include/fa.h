@@ -117,8 +117,12 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 /* Bytes of device workspace fa_backward needs for B sequences of at most N
  * tokens with H heads of size d: two fp32 [B*N, H] arrays, each rounded up
  * to 256 bytes, the row terms D = rowsum(dO * O) and lse * log2(e) (written
- * by the query-side kernel, read by the key-side kernel).  Returns 0 if the
- * size overflows.  Host-only, never fails otherwise. */
+ * by the query-side kernel, read by the key-side kernel).  The size depends
+ * on the token count B*N only (d is accepted for symmetry), so a caller that
+ * counts tokens T may ask for (1, T, H, d); for packed variable-length
+ * input that T must be B*max_seqlen, the bound fa_backward checks against
+ * (it cannot read cu_seqlens on the host).  Returns 0 if the size overflows.
+ * Host-only, never fails otherwise. */
 size_t fa_backward_workspace_size(int B, int N, int H, int d);
 
 /* Backward pass (recomputation from lse, lab write-up section 3.3).
@@ -217,6 +221,59 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
                                    void* workspace, size_t workspace_bytes,
                                    const uint8_t* block_mask);
 
+/* ---------------------------------------------------- stored dropout bits
+ * Dropout (lab write-up section 2.3: the mask is regenerated, not stored) as
+ * fa_forward / fa_backward draw it costs each of the three kernels the
+ * Philox-4x32-10 hashing of every element.  These calls trade memory for
+ * that work: the forward stores the keep decisions it draws, one bit per
+ * (query, key) pair, and the backward reads them instead of hashing again.
+ * Results are bitwise those of fa_forward / fa_backward with the same
+ * arguments.  Dense and packed variable-length input only (no block mask).
+ *
+ * Layout of keep_bits (DEVICE, 32-bit words, caller-owned): with Np = N
+ * rounded up to a multiple of 4, word
+ *   (((b * H + h) * ceil(N/64) + t) * 2 + w) * Np + i
+ * holds in bit k the decision for query i against key 64 t + 32 w + k of
+ * sequence b, head h (local indices; 1 = kept), i.e. Np * ceil(N/64) * 8
+ * bytes per (b, h).  The forward writes the words of every tile a query
+ * computes (up to its causal diagonal and the sequence end) and leaves the
+ * others as they were; the backward reads no other. */
+
+/* Bytes of keep_bits for B sequences of at most N tokens with H heads.
+ * Returns 0 for N > FA_MASK_MAX_N (a head's bits must fit one 32-bit
+ * buffer range) or sizes that overflow.  Host-only. */
+size_t fa_dropout_bits_size(int B, int N, int H);
+
+/* fa_forward, storing its dropout decisions into keep_bits (16-byte
+ * aligned, keep_bits_bytes >= fa_dropout_bits_size(B, N, H)).  With
+ * dropout_p == 0 it is exactly fa_forward and keep_bits is not touched (it
+ * may be NULL).  Errors: those of fa_forward; FA_ERR_NULL_POINTER (NULL
+ * keep_bits with dropout), FA_ERR_WORKSPACE (keep_bits_bytes too small),
+ * FA_ERR_ALIGNMENT, FA_ERR_UNSUPPORTED (N > FA_MASK_MAX_N with dropout). */
+int fa_forward_keep(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream,
+                    int dtype, int64_t ld_qkv, uint32_t* keep_bits, size_t keep_bits_bytes);
+
+/* fa_backward, reading the dropout decisions from keep_bits as
+ * fa_forward_keep wrote them for the same shapes, cu_seqlens, dropout_p and
+ * seed (the seed is then unused).  With dropout_p == 0 it is exactly
+ * fa_backward.  Errors: those of fa_backward and of fa_forward_keep. */
+int fa_backward_keep(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                     float scale, int causal, const int32_t* cu_seqlens, float dropout_p,
+                     uint64_t seed, void* stream, int dtype, int64_t ld_qkv, void* workspace,
+                     size_t workspace_bytes, const uint32_t* keep_bits, size_t keep_bits_bytes);
+
+/* One of the two kernels of fa_backward_keep (stage 0: D and dQ, stage 1: dK
+ * and dV), as fa_backward_stage is for fa_backward. */
+int fa_backward_keep_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
+                           int N, int d, float scale, int causal, const int32_t* cu_seqlens,
+                           float dropout_p, uint64_t seed, void* stream, int dtype, int64_t ld_qkv,
+                           void* workspace, size_t workspace_bytes, const uint32_t* keep_bits,
+                           size_t keep_bits_bytes);
+
 /* ------------------------------------------------------ KV-cache decode
  * One decode step of inference with a KV cache (lab write-up, section 6.1):
  * nq new query tokens of each sequence attend to that sequence's cached keys
@@ -278,8 +335,13 @@ int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, con
 /* Dropout keep mask of a single (b, h) head as the fused kernels draw it:
  * keep[i * N + j] = 1 if element (i, j) is kept, 0 if dropped, for
  * 0 <= i, j < N (both local indices; causal masking is NOT applied).  keep
- * is a device buffer of N*N bytes.  Exposes the kernels' hash so that tests
- * can compare it bit for bit with an independent implementation. */
+ * is a device buffer of N*N bytes.  The decision for (i, j) depends on
+ * (seed, b, h, i, j) only, not on N, so for packed variable-length input
+ * the mask of sequence s is this call with b = s and N = its length (its
+ * top-left L x L block for any larger N).  Exposes the kernels' hash so
+ * that tests can compare it bit for bit with an independent implementation;
+ * a full [B, H, N, N] export is not offered (at 16 sequences of 4096 tokens
+ * and 32 heads it would be 8.6 GB of bytes). */
 int fa_dropout_mask(uint8_t* keep, int b, int h, int N, float dropout_p, uint64_t seed,
                     void* stream);
 

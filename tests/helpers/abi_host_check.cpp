@@ -101,6 +101,44 @@ int main() {
   CHECK(fa_backward_stage(1, P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.f, 0, nullptr, 1, 0, P,
                           need) == FA_OK);
   CHECK(last_stages == 2);
+  // stored dropout bits: size, checks, and the buffer reaching the launchers
+  // only with dropout
+  const size_t kneed = fa_dropout_bits_size(2, 100, 3);
+  CHECK(kneed == (size_t)2 * 3 * 2 * 2 * 100 * 4);  // ceil(100/64) = 2 tiles of two words per query
+  CHECK(fa_dropout_bits_size(1, FA_MASK_MAX_N, 1) == (size_t)FA_MASK_MAX_N / 64 * 2 * FA_MASK_MAX_N * 4);
+  CHECK(fa_dropout_bits_size(1, 101, 1) == (size_t)2 * 2 * 104 * 4);  // rows padded to a multiple of 4
+  CHECK(fa_dropout_bits_size(1, FA_MASK_MAX_N + 1, 1) == 0 && fa_dropout_bits_size(0, 8, 1) == 0);
+  CHECK(fa_dropout_bits_size(1 << 30, 65536, 1 << 30) == 0);  // overflow
+  uint32_t* KB = static_cast<uint32_t*>(P);
+  CHECK(fa_forward_keep(P, P, P, P, F, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 7, nullptr, 1, 0, KB, kneed) == FA_OK);
+  CHECK(last.keep_bits == KB && last.dropout);
+  CHECK(fa_forward_keep(P, P, P, P, F, 2, 3, 100, 64, 1.f, 1, nullptr, 0.f, 7, nullptr, 1, 0, nullptr, 0) == FA_OK);
+  CHECK(last.keep_bits == nullptr);
+  CHECK(fa_forward(P, P, P, P, F, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 7, nullptr, 1, 0) == FA_OK);
+  CHECK(last.keep_bits == nullptr);
+  const int kb_before = calls;
+  CHECK(fa_forward_keep(P, P, P, P, F, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 7, nullptr, 1, 0, nullptr, kneed) ==
+        FA_ERR_NULL_POINTER);
+  CHECK(fa_forward_keep(P, P, P, P, F, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 7, nullptr, 1, 0, KB, kneed - 1) ==
+        FA_ERR_WORKSPACE);
+  CHECK(fa_forward_keep(P, P, P, P, F, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 7, nullptr, 1, 0, KB + 1, kneed) ==
+        FA_ERR_ALIGNMENT);
+  CHECK(fa_forward_keep(P, P, P, P, F, 1, 1, FA_MASK_MAX_N + 64, 64, 1.f, 1, nullptr, 0.1f, 7, nullptr, 1, 0, KB,
+                        (size_t)1 << 40) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_backward_keep(P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 0, nullptr, 1, 0, P, need,
+                         KB, kneed - 4) == FA_ERR_WORKSPACE);
+  CHECK(fa_backward_keep_stage(2, P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 0, nullptr, 1, 0,
+                               P, need, KB, kneed) == FA_ERR_BAD_ARGUMENT);
+  CHECK(calls == kb_before);
+  CHECK(fa_backward_keep(P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 0, nullptr, 1, 0, P, need,
+                         KB, kneed) == FA_OK);
+  CHECK(last.keep_bits == KB && last_stages == 3);
+  CHECK(fa_backward_keep_stage(0, P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 0, nullptr, 1, 0,
+                               P, need, KB, kneed) == FA_OK);
+  CHECK(last.keep_bits == KB && last_stages == 1);
+  CHECK(fa_backward(P, P, P, P, F, P, P, P, P, 2, 3, 100, 64, 1.f, 1, nullptr, 0.1f, 0, nullptr, 1, 0, P, need) ==
+        FA_OK);
+  CHECK(last.keep_bits == nullptr);
   // no-allocation backward: every argument check, then the scratch limit,
   // all before any HIP call (a valid call needs a GPU and is not made here)
   const int launches = calls;

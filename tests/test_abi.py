@@ -28,10 +28,11 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage", "fa_backward_noalloc",
-        "fa_backward_stage",
-        "fa_backward_workspace_size", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size", "fa_dropout_mask",
-        "fa_forward", "fa_forward_block_sparse", "fa_strerror"])
+        "fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_stage", "fa_backward_keep",
+        "fa_backward_keep_stage", "fa_backward_noalloc", "fa_backward_stage",
+        "fa_backward_workspace_size", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size",
+        "fa_dropout_bits_size", "fa_dropout_mask", "fa_forward", "fa_forward_block_sparse", "fa_forward_keep",
+        "fa_strerror"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -62,6 +63,11 @@ def lib():
     L.fa_decode_workspace_size.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
     L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, i, vp, ctypes.c_size_t]
+    L.fa_dropout_bits_size.argtypes = [i, i, i]
+    L.fa_dropout_bits_size.restype = ctypes.c_size_t
+    L.fa_forward_keep.argtypes = L.fa_forward.argtypes + [vp, ctypes.c_size_t]
+    L.fa_backward_keep.argtypes = L.fa_backward.argtypes + [vp, ctypes.c_size_t]
+    L.fa_backward_keep_stage.argtypes = [i] + L.fa_backward_keep.argtypes
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     return L
@@ -119,6 +125,26 @@ def test_workspace_size_edge_cases(lib):
     assert lib.fa_backward_workspace_size(0, 1, 1, 64) == 0
     assert lib.fa_backward_workspace_size(1, 1, 1, 64) > 0
     assert lib.fa_backward_workspace_size(2**31 - 1, 2**31 - 1, 2**31 - 1, 128) == 0   # overflow
+
+
+def test_dropout_bits_checks(lib):
+    # one bit per (query, key) pair, keys padded to 64 per query
+    assert lib.fa_dropout_bits_size(2, 100, 3) == 2 * 3 * 100 * 128 // 8
+    assert lib.fa_dropout_bits_size(1, 4096, 1) == 4096 * 4096 // 8
+    assert lib.fa_dropout_bits_size(1, 101, 1) == 2 * 2 * 104 * 4   # rows padded to a multiple of 4
+    assert lib.fa_dropout_bits_size(1, 65537, 1) == 0
+    assert lib.fa_dropout_bits_size(0, 64, 1) == 0
+    need = lib.fa_backward_workspace_size(1, 128, 2, 64)
+    kneed = lib.fa_dropout_bits_size(1, 128, 2)
+    fargs = [P, P, P, P, P, 1, 2, 128, 64, 0.125, 1, None, 0.1, 3, None, 1, 0]
+    assert lib.fa_forward_keep(*fargs, None, kneed) == 1
+    assert lib.fa_forward_keep(*fargs, P, kneed - 1) == 6
+    assert lib.fa_forward_keep(*fargs, P + 4, kneed) == 5
+    bargs = [P] * 9 + [1, 2, 128, 64, 0.125, 1, None, 0.1, 3, None, 1, 0, P, need]
+    assert lib.fa_backward_keep(*bargs, None, kneed) == 1
+    assert lib.fa_backward_keep(*bargs, P, 0) == 6
+    assert lib.fa_backward_keep_stage(5, *bargs, P, kneed) == 4
+    assert lib.fa_backward_keep(*bargs[:12], 80, *bargs[13:], P, kneed) == 3
 
 
 def test_dropout_mask_checks(lib):

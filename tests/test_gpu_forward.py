@@ -127,7 +127,20 @@ def test_forward_writes_only_its_outputs():
 
 def test_dropout_mask_bit_exact():
     import exact_tiled_attention_40_amd as fa
-    for (b, h, N, p, seed) in [(0, 0, 128, 0.1, 1001), (3, 7, 77, 0.5, 2**40 + 3), (15, 31, 300, 0.1, 1005)]:
+    wl = workloads.WORKLOADS["varlen16_H32_d128_bf16_causal_p0.1"]
+    for (b, h, N, p, seed) in [(0, 0, 128, 0.1, 1001), (3, 7, 77, 0.5, 2**40 + 3), (15, 31, 300, 0.1, 1005),
+                               (15, 31, 4096, wl.dropout_p, wl.seed)]:
         m = fa.fa_dropout_mask(b, h, N, p, seed).cpu().numpy()
         ref = oracle.keep_mask(seed, p, b, h, N)
         assert np.array_equal(m, ref), (b, h, N)
+
+
+def test_dropout_mask_independent_of_length():
+    """The keep decision of (i, j) depends on (seed, b, h, i, j) only: the
+    mask of a shorter sequence is the top-left block of a longer one's (the
+    export of a packed variable-length sequence relies on it)."""
+    import exact_tiled_attention_40_amd as fa
+    for (b, h, n_small, n_big, p, seed) in [(5, 2, 100, 300, 0.2, 77), (15, 31, 1, 4096, 0.1, 1005)]:
+        small = fa.fa_dropout_mask(b, h, n_small, p, seed).cpu().numpy()
+        big = fa.fa_dropout_mask(b, h, n_big, p, seed).cpu().numpy()
+        assert np.array_equal(big[:n_small, :n_small], small), (b, h, n_small, n_big)
