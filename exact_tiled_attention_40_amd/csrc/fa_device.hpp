@@ -72,19 +72,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // at lds_base + 16*l (lds_base must be wave-uniform).  Issued from inline
 // assembly so that the compiler does not wait for it before unrelated LDS
 // reads (it cannot tell the double buffers apart); callers wait with
-// wait_vmem() before a barrier.  M0 (the LDS base register) is restored.
+// wait_vmem() before a barrier.  M0 (the LDS base register) is declared
+// clobbered, so the compiler sets it again wherever it needs it itself.
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voffset) {
   const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
       : "s"(base), "v"(voffset), "s"(r)
-      : "memory");
+      : "memory", "m0");
 }
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
@@ -92,32 +90,26 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 
 __device__ __forceinline__ void buffer_load_lds16_addr(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voffset) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
       : "s"(lds_base), "v"(voffset), "s"(r)
-      : "memory");
+      : "memory", "m0");
 }
 
 // 4-byte buffer load of every lane straight into LDS: lane l's 4 bytes land
 // at lds_base + 4*l.  Same conventions as buffer_load_lds16.
 __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voffset) {
   const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
       : "s"(base), "v"(voffset), "s"(r)
-      : "memory");
+      : "memory", "m0");
 }
 
 // A tile of ROWS rows of D 16-bit elements in LDS, without padding.  The
@@ -166,16 +158,13 @@ __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
 
 // buffer_load_lds4 with the LDS destination given as a byte address.
 __device__ __forceinline__ void buffer_load_lds4_addr(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voffset) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
       : "s"(lds_base), "v"(voffset), "s"(r)
-      : "memory");
+      : "memory", "m0");
 }
 
 // MI355X: 8 XCDs, each with its own L2; the hardware deals a launch's

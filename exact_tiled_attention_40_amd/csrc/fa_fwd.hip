@@ -422,11 +422,13 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
   // the K tile at position k+2 into buffer k % 2, then of the V tile at
   // position k+1 into buffer (k+1) % 2 (both buffers were last read in slot
   // 2k).  tk1, tk2 = tile indices at positions k+1, k+2 (or -1).
-  auto load_part = [&](int k, int tk1, int tk2, int u) __attribute__((always_inline)) {
+  // wv: the wave whose share is loaded (a group-1 wave also loads its
+  // group-0 partner's when kG1Loads).
+  auto load_part = [&](int k, int tk1, int tk2, int u, int wv) __attribute__((always_inline)) {
     constexpr int per = kPer;
     const bool isk = u < per;
-    const int blk = (isk ? u : u - per) * kWaves + w;
-    if (blk >= T::kBlocks) return;
+    const int blk = (isk ? u : u - per) * kWaves + wv;
+    if (T::kBlocks % kWaves != 0 && blk >= T::kBlocks) return;
     const int tt = isk ? tk2 : tk1;
     if (tt < 0) return;
     const int j0 = tt * kBC;
@@ -440,7 +442,10 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
   // The loop for one group G, whose wave-level schedule is fixed at compile
   // time: group 0 spreads its loads of slot 2k + 1 between the products of
   // M(k), group 1 through the softmax of V(k), so that no wave stalls on a
-  // burst of load issues.
+  // burst of load issues.  At d = 128 group 1 issues both groups' loads and
+  // group 0's matrix phases issue none (2-4 % faster there; at d = 32 and 96,
+  // where the softmax phase is the longer one, 3-6 % slower).
+  constexpr bool kG1Loads = kWaves == 8 && D == 128;
   auto run = [&](auto G) __attribute__((always_inline)) {
     constexpr int g = decltype(G)::value;
     // the wave computes the visited tiles up to its last one: a prefix
@@ -455,13 +460,16 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
     for (; tk1 >= 0 && tk1 <= last; ++k) {
       const int tk2 = tile_or_none(k + 2);
       const bool skip = skip_at(k);
-      auto loads = [&](int u) { load_part(k, tk1, tk2, u); };
+      auto loads = [&](int u) {
+        load_part(k, tk1, tk2, u, w);
+        if constexpr (kG1Loads) load_part(k, tk1, tk2, u, w - 4);
+      };
       if constexpr (g == 1) v_phase(tk, false, skip, loads);
       else v_phase(tk, false, skip, no_hook);
       if (g == 0 && k > 0) wait_vmem();
       __syncthreads();
       kb_flush();
-      if constexpr (g == 0) m_phase(k, true, loads);
+      if constexpr (g == 0 && !kG1Loads) m_phase(k, true, loads);
       else m_phase(k, true, no_hook);
       if (g == 1) wait_vmem();
       __syncthreads();
@@ -474,13 +482,16 @@ __global__ __launch_bounds__((64 * waves<SPARSE, D>()), (wgs_per_cu<SPARSE, D>()
       const int tk2 = tile_or_none(k + 2);
       const bool mine = tk <= last;
       if (g == 1)
-        for (int u = 0; u < kLoads; ++u) load_part(k, tk1, tk2, u);
+        for (int u = 0; u < kLoads; ++u) {
+          load_part(k, tk1, tk2, u, w);
+          if constexpr (kG1Loads) load_part(k, tk1, tk2, u, w - 4);
+        }
       if (mine) v_phase(tk, true, skip_at(k), no_hook);
       if (g == 0 && k > 0) wait_vmem();
       __syncthreads();
       if (mine) kb_flush();
-      if (g == 0)
-        for (int u = 0; u < kLoads; ++u) load_part(k, tk1, tk2, u);
+      if (g == 0 && !kG1Loads)
+        for (int u = 0; u < kLoads; ++u) load_part(k, tk1, tk2, u, w);
       if (mine) m_phase(k, false, no_hook);
       if (g == 1) wait_vmem();
       __syncthreads();
