@@ -235,9 +235,11 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
  *   (((b * H + h) * ceil(N/64) + t) * 2 + w) * Np + i
  * holds in bit k the decision for query i against key 64 t + 32 w + k of
  * sequence b, head h (local indices; 1 = kept), i.e. Np * ceil(N/64) * 8
- * bytes per (b, h).  The forward writes the words of every tile a query
- * computes (up to its causal diagonal and the sequence end) and leaves the
- * others as they were; the backward reads no other. */
+ * bytes per (b, h).  The forward writes the words of the key tiles it
+ * computes for each query (at least up to the query's causal diagonal, and
+ * only rows of real queries) and leaves the others as they were; the
+ * backward also reads some unwritten words, but only for pairs the causal
+ * mask or the sequence end hides, whose bits have no effect. */
 
 /* Bytes of keep_bits for B sequences of at most N tokens with H heads.
  * Returns 0 for N > FA_MASK_MAX_N (a head's bits must fit one 32-bit
