@@ -222,11 +222,14 @@ int fa_backward_block_sparse_stage(int stage, const void* q, const void* k, cons
                                    const uint8_t* block_mask);
 
 /* ---------------------------------------------------- stored dropout bits
- * Dropout (lab write-up section 2.3: the mask is regenerated, not stored) as
- * fa_forward / fa_backward draw it costs each of the three kernels the
- * Philox-4x32-10 hashing of every element.  These calls trade memory for
- * that work: the forward stores the keep decisions it draws, one bit per
- * (query, key) pair, and the backward reads them instead of hashing again.
+ * Dropout, which the coreui.cn FlashAttention-2 how-to (section 2.3) singles
+ * out for special handling, is drawn by fa_forward / fa_backward from a
+ * counter-based hash in each of the three kernels, in the spirit of the lab
+ * write-up's section 3.3 (the backward recomputes rather than stores N x N
+ * intermediates).  These calls trade memory for that hashing: the forward
+ * stores the keep decisions it draws, one bit per (query, key) pair (N^2/8
+ * bytes per head, against 2 N^2 for a stored 16-bit P), and the backward
+ * reads them instead of hashing again.
  * Results are bitwise those of fa_forward / fa_backward with the same
  * arguments.  Dense and packed variable-length input only (no block mask).
  *
