@@ -15,13 +15,19 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="n
 
 
 def run(fa, q, k, v, do, out, **kw):
-    o, lse, dq, dk, dv, ws = out
-    fa.fa_forward(q, k, v, out=o, lse=lse, **kw)
-    fa.fa_backward(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    o, lse, dq, dk, dv, ws, kb = out
+    if kb is None:
+        fa.fa_forward(q, k, v, out=o, lse=lse, **kw)
+        fa.fa_backward(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    else:
+        fa.fa_forward_keep(q, k, v, keep_bits=kb, out=o, lse=lse, **kw)
+        fa.fa_backward_keep(q, k, v, o, lse, do, keep_bits=kb, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
 
 
-@pytest.mark.parametrize("dropout_p", [0.0, 0.2])
-def test_side_stream_and_graph_replay_match_eager(dropout_p):
+# dropout with the hashing calls, and with the stored-keep-bit calls (whose
+# bit buffer is cleared before every replay as well)
+@pytest.mark.parametrize("dropout_p,keep", [(0.0, False), (0.2, False), (0.2, True)])
+def test_side_stream_and_graph_replay_match_eager(dropout_p, keep):
     import exact_tiled_attention_40_amd as fa
     x = workloads.custom(2, 3, 300, 128, "bf16", True, dropout_p=dropout_p, seed=81)
     q, k, v, do, _ = to_gpu(x)
@@ -29,8 +35,9 @@ def test_side_stream_and_graph_replay_match_eager(dropout_p):
 
     def buffers():
         ws = torch.empty(fa.fa_backward_workspace_size(2, 300, 3, 128), dtype=torch.uint8, device="cuda")
+        kb = torch.zeros(fa.fa_dropout_bits_size(2, 300, 3), dtype=torch.uint8, device="cuda") if keep else None
         return (torch.empty_like(q), torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda"),
-                torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), ws)
+                torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), ws, kb)
 
     ref = buffers()
     run(fa, q, k, v, do, ref, **kw)
@@ -59,12 +66,14 @@ def test_side_stream_and_graph_replay_match_eager(dropout_p):
     with torch.cuda.graph(g, stream=capture_stream):
         run(fa, q, k, v, do, cap, **kw)
     for rep in range(4):
-        for t in cap[:5]:
+        for t in cap[:5] + ((cap[6],) if keep else ()):
             t.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for a, b in zip(ref[:5], cap[:5]):
             assert torch.equal(a, b), rep
+        if keep:
+            assert torch.equal(ref[6], cap[6]), rep
         # unrelated eager work between replays
         (q.float() * 2).sum().item()
