@@ -68,27 +68,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// 16-byte buffer load of every lane straight into LDS: lane l's 16 bytes land
-// at lds_base + 16*l (lds_base must be wave-uniform).  Issued from inline
-// assembly so that the compiler does not wait for it before unrelated LDS
-// reads (it cannot tell the double buffers apart); callers wait with
-// wait_vmem() before a barrier.  M0 (the LDS base register) is declared
-// clobbered, so the compiler sets it again wherever it needs it itself.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voffset) {
-  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(base), "v"(voffset), "s"(r)
-      : "memory", "m0");
-}
-
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
 }
 
+// 16-byte buffer load of every lane straight into LDS: lane l's 16 bytes land
+// at byte address lds_base + 16*l (lds_base must be wave-uniform).  Issued
+// from inline assembly so that the compiler does not wait for it before
+// unrelated LDS reads (it cannot tell the double buffers apart); callers wait
+// with wait_vmem() before a barrier.  M0 (the LDS base register) is declared
+// clobbered, so the compiler sets it again wherever it needs it itself.
 __device__ __forceinline__ void buffer_load_lds16_addr(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voffset) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -100,7 +89,7 @@ __device__ __forceinline__ void buffer_load_lds16_addr(__amdgpu_buffer_rsrc_t r,
 }
 
 // 4-byte buffer load of every lane straight into LDS: lane l's 4 bytes land
-// at lds_base + 4*l.  Same conventions as buffer_load_lds16.
+// at lds_base + 4*l.  Same conventions as buffer_load_lds16_addr.
 __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voffset) {
   const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
   asm volatile(
@@ -111,31 +100,6 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, const
       : "s"(base), "v"(voffset), "s"(r)
       : "memory", "m0");
 }
-
-// A tile of ROWS rows of D 16-bit elements in LDS, without padding.  The
-// 16-byte chunk c of row r is stored at chunk position c ^ swz(r): the 16
-// rows read together by a b128 read land in 16 different chunk positions,
-// and the 4 rows read together by a transpose read in 4 different chunk
-// pairs.  The tile is filled by 1 KB direct-to-LDS loads (64 lanes x 16 B).
-template <int D, int ROWS>
-struct SwzTile {
-  static constexpr int kCPR = D / 8;               // 16-byte chunks per row
-  static constexpr int kElems = ROWS * D;
-  static constexpr int kLoads = ROWS * kCPR / 64;  // 1 KB loads per tile
-  __device__ static __forceinline__ int swz(int r) { return ((r & (kCPR / 2 - 1)) << 1) | ((r / (kCPR / 2)) & 1); }
-  // element offset of (row r, element col)
-  __device__ static __forceinline__ int at(int r, int col) { return r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7); }
-  // Load number u (0 <= u < kLoads) of the tile: lane l fills chunk position
-  // p = 64u + l, i.e. row p / kCPR, from global row r (row_bytes apart) of
-  // the buffer r.  Rows the buffer range does not cover read as zeros.
-  __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint16_t* tile, uint32_t row_bytes, int u,
-                                              int lane) {
-    const int p = u * 64 + lane;
-    const int r = p / kCPR;
-    const int c = (p % kCPR) ^ swz(r);
-    buffer_load_lds16(rsrc, tile + u * 512, (uint32_t)r * row_bytes + 16 * c);
-  }
-};
 
 // LDS address (bytes) of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
