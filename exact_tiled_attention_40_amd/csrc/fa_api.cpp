@@ -354,10 +354,10 @@ const char* fa_strerror(int code) {
     case FA_OK: return "success";
     case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "B, H and N must be >= 1 (and B*N tokens must fit in int32)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dim (32, 64, 96, 128, 160, 192 or 256), dtype (fp16 or bf16) or block-sparse length";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim (32, 64, 96, 128, 160, 192 or 256), dtype (fp16 or bf16), or length for block masks / stored keep bits";
     case FA_ERR_BAD_ARGUMENT: return "scale must be finite and > 0, dropout_p in [0, 1)";
     case FA_ERR_ALIGNMENT: return "pointers must be 16-byte aligned, ld_qkv a multiple of 8 and >= H*d";
-    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
+    case FA_ERR_WORKSPACE: return "workspace (or keep-bit buffer) missing or smaller than fa_backward_workspace_size() (fa_dropout_bits_size())";
     case FA_ERR_HIP: return "a HIP kernel launch failed";
     case FA_ERR_SCRATCH_LIMIT: return "B*N*H exceeds FA_NOALLOC_MAX_ROWS, the fixed scratch of fa_backward_noalloc";
     default: return "unknown fa status code";

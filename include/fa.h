@@ -94,10 +94,11 @@ enum fa_status {
     FA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
     FA_ERR_BAD_SHAPE = 2,      /* B, H or N < 1, or a size overflows */
     FA_ERR_UNSUPPORTED = 3,    /* d not in {32, 64, 96, 128, 160, 192, 256}, unknown dtype,
-                                  or a block-sparse N above FA_MASK_MAX_N */
+                                  or N above FA_MASK_MAX_N for a block-sparse call or a
+                                  stored-keep-bit call with dropout */
     FA_ERR_BAD_ARGUMENT = 4,   /* scale not finite, dropout_p not in [0, 1) */
     FA_ERR_ALIGNMENT = 5,      /* pointer not 16-byte aligned or bad ld_qkv */
-    FA_ERR_WORKSPACE = 6,      /* workspace NULL or smaller than required */
+    FA_ERR_WORKSPACE = 6,      /* workspace (or keep-bit buffer) NULL or smaller than required */
     FA_ERR_HIP = 7,            /* a HIP launch reported an error */
     FA_ERR_SCRATCH_LIMIT = 8   /* fa_backward_noalloc: B*N*H above FA_NOALLOC_MAX_ROWS */
 };
