@@ -148,3 +148,38 @@ def test_keep_bits_varlen_workload_shape():
             ref = oracle.keep_mask(wl.seed, wl.dropout_p, s, h, L).astype(bool)
             assert int((got[vis] != ref[vis]).sum()) == 0, (s, h)
             print(f"[varlen workload seq {s} head {h} L={L}] bits equal, kept {ref[vis].mean():.4f}", flush=True)
+
+
+def test_keep_bits_at_the_longest_sequence():
+    """One sequence of FA_MASK_MAX_N = 65536 tokens (the largest the keep-bit
+    buffer addresses: 512 MiB per head), causal, p = 0.1: every output
+    bitwise equal to the hashing path, and the stored bits of the first 4096
+    queries against the first 4096 keys equal to the oracle's keep mask (a
+    decision depends on (seed, b, h, i, j) only, so the oracle's mask of a
+    4096-token sequence covers them)."""
+    import exact_tiled_attention_40_amd as fa
+    N, H, d, p, seed = fa.FA_MASK_MAX_N, 1, 64, 0.1, 4242
+    q, k, v, do, kw = _inputs([N], H, d, "bf16", False, seed)
+    kw.update(causal=True, dropout_p=p, seed=seed)
+    need = fa.fa_dropout_bits_size(1, N, H)
+    assert need == N * (N // 64) * 8
+    buf = _garbage(need, 5)
+    guard = buf[need:].clone()
+    o_ref, lse_ref = fa.fa_forward(q, k, v, **kw)
+    o, lse = fa.fa_forward_keep(q, k, v, keep_bits=buf[:need], **kw)
+    g_ref = fa.fa_backward(q, k, v, o_ref, lse_ref, do, **kw)
+    g = fa.fa_backward_keep(q, k, v, o, lse, do, keep_bits=buf[:need], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    assert torch.equal(buf[need:], guard)
+    for name, a, r in zip(("dQ", "dK", "dV"), g, g_ref):
+        assert torch.equal(a, r), name
+    L = 4096
+    words = buf[:need].view(torch.int32).view(N // 64, 2, N)[: L // 64, :, :L].cpu().numpy().view(np.uint32)
+    per_query = np.ascontiguousarray(words.transpose(2, 0, 1))  # [L, L/64, 2]
+    got = np.unpackbits(per_query.view(np.uint8), bitorder="little").reshape(L, L).astype(bool)
+    ref = oracle.keep_mask(seed, p, 0, 0, L).astype(bool)
+    vis = np.tril(np.ones((L, L), bool))
+    assert int((got[vis] != ref[vis]).sum()) == 0
+    print(f"[keep bits N={N}] outputs bitwise equal; first {L} rows' bits equal the oracle, kept "
+          f"{ref[vis].mean():.4f}", flush=True)
